@@ -1,0 +1,223 @@
+"""Plain, slow, fp64 CPU oracle of the Top-p block-sparse attention hot path.
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, the smoke check and the CPU
+baseline of the benchmark; never by the GPU library.  It shares no code with
+the HIP kernels.  Every function works on numpy arrays in float64 and follows
+the pages step by step, using numpy primitives (mean, matmul, exp, a stable
+argsort, cumsum) and no blocking, fusion or reordering of its own.
+
+Sources (titles of the web pages the method is taken from):
+  [FVAttn]  "腾讯+中山大学新作：视频生成提速2.11×，靠的是RLB和SASA" (PaperDaily summary
+            of FVAttn, arXiv:2607.16190), section "AI视频生成的阿喀琉斯之踵", the
+            paragraph describing Top-p routing; and the RLB section (per-head load).
+  [TUTOR]   the engineering tutorial page on accelerating video generation, section
+            5.2 "块稀疏注意力的教学实现" (block mean-pooling, 1/sqrt(d) block scores)
+            and section 5.3 "正确性验证" (full coverage must equal dense attention).
+
+Readings of points the pages leave open (each also listed in the design notes):
+  * importance of key block j for query block i = softmax over j of the scaled
+    pooled score  qbar_i . kbar_j / sqrt(d)  (pooled form of [TUTOR] 5.2, with the
+    softmax that turns scores into a mass summing to 1, as [FVAttn] accumulates
+    "importance" up to p);
+  * pooling is the mean over the block's REAL tokens (the ragged last block is
+    divided by its own length; padding never enters);
+  * "reaches p" means cumulative mass >= p; the kept set is the shortest prefix
+    of the descending order that reaches p; ties in importance go to the lower
+    block index; p >= 1 keeps every block, and if rounding leaves the total below
+    p every block is kept;
+  * routing is per (head, query block): all tokens of a query block share the
+    kept set;
+  * attention is exact, non-causal softmax attention with scale 1/sqrt(d) over
+    the real tokens of the kept key blocks.
+"""
+from __future__ import annotations
+
+import math
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+
+# --------------------------------------------------------------------------
+# Step 1: fixed-size blocks ([FVAttn] Top-p paragraph: keys/values are cut into
+# fixed blocks of e.g. 32 or 64 tokens).
+# --------------------------------------------------------------------------
+def block_bounds(n_tokens: int, block: int) -> List[tuple]:
+    """[(start, end)] of the consecutive blocks of `block` tokens; the last may be short."""
+    nb = -(-n_tokens // block)
+    return [(i * block, min((i + 1) * block, n_tokens)) for i in range(nb)]
+
+
+# --------------------------------------------------------------------------
+# Step 2: block mean-pooling ([TUTOR] 5.2: each block is summarised by the mean
+# vector of its tokens, which keeps the scoring cheap).
+# --------------------------------------------------------------------------
+def pool_blocks(x: np.ndarray, block: int) -> np.ndarray:
+    """x [N, d] -> [nb, d]: mean over the real tokens of each block."""
+    x = np.asarray(x, dtype=np.float64)
+    return np.stack([x[s:e].mean(axis=0) for s, e in block_bounds(x.shape[0], block)])
+
+
+# --------------------------------------------------------------------------
+# Step 3: scaled block scores ([TUTOR] 5.2: pooled-q . pooled-k divided by sqrt(d)).
+# --------------------------------------------------------------------------
+def block_scores(qbar: np.ndarray, kbar: np.ndarray) -> np.ndarray:
+    d = qbar.shape[1]
+    return (qbar @ kbar.T) / math.sqrt(d)
+
+
+# --------------------------------------------------------------------------
+# Step 4: importance = softmax over key blocks (max subtracted), rows sum to 1.
+# --------------------------------------------------------------------------
+def block_importance(scores: np.ndarray) -> np.ndarray:
+    m = scores.max(axis=-1, keepdims=True)
+    e = np.exp(scores - m)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+# --------------------------------------------------------------------------
+# Step 5: descending order of importance, ties to the lower block index
+# ([FVAttn]: blocks are ranked by importance in descending order).  A stable
+# sort on -P keeps equal keys in ascending index order.
+# --------------------------------------------------------------------------
+def routing_order(P: np.ndarray) -> np.ndarray:
+    return np.argsort(-P, axis=-1, kind="stable")
+
+
+# --------------------------------------------------------------------------
+# Step 6: the Top-p cut ([FVAttn]: blocks are taken in that order until the
+# cumulative importance reaches p; the kept set is the smallest such set).
+# --------------------------------------------------------------------------
+def topp_count(P_sorted_row: np.ndarray, p: float) -> int:
+    """k* = smallest k >= 1 with sum of the first k sorted masses >= p.
+    p >= 1, or a total that rounding leaves below p, keeps every block."""
+    n = P_sorted_row.shape[0]
+    if p >= 1.0:
+        return n
+    S = np.cumsum(P_sorted_row)          # S[k-1] = mass of the first k blocks
+    hit = np.nonzero(S >= p)[0]
+    return int(hit[0]) + 1 if hit.size else n
+
+
+def route_head(q_h: np.ndarray, k_h: np.ndarray, block_q: int, block_k: int, p: float,
+               diagnostics: bool = False):
+    """Routing of one head: q_h, k_h [N, d].  Returns (kept, extra) where kept is a
+    list over query blocks of ascending int arrays of kept key-block indices.
+    With diagnostics, extra = dict(order, cum, counts, P)."""
+    qbar = pool_blocks(q_h, block_q)
+    kbar = pool_blocks(k_h, block_k)
+    P = block_importance(block_scores(qbar, kbar))
+    order = routing_order(P)
+    kept, counts, cums = [], [], []
+    for i in range(P.shape[0]):
+        Ps = P[i, order[i]]
+        c = topp_count(Ps, p)
+        kept.append(np.sort(order[i, :c]).astype(np.int64))
+        counts.append(c)
+        if diagnostics:
+            cums.append(np.cumsum(Ps))
+    extra = None
+    if diagnostics:
+        extra = dict(order=order, cum=np.array(cums), counts=np.array(counts), P=P,
+                     qbar=qbar, kbar=kbar)
+    return kept, extra
+
+
+def csr_rows(kept_per_head: Sequence[Sequence[np.ndarray]]):
+    """Build the CSR of key-block indices over rows r = head * nqb + i, plus the
+    per-head load ([FVAttn] RLB section: a head's load is the number of blocks it
+    must compute, read off its sparse mask)."""
+    counts = [len(k) for head in kept_per_head for k in head]
+    row_ptr = np.zeros(len(counts) + 1, dtype=np.int64)
+    row_ptr[1:] = np.cumsum(counts)
+    col_idx = (np.concatenate([k for head in kept_per_head for k in head]).astype(np.int64)
+               if counts and row_ptr[-1] > 0 else np.zeros(0, dtype=np.int64))
+    head_load = np.array([sum(len(k) for k in head) for head in kept_per_head], dtype=np.int64)
+    return row_ptr, col_idx, head_load
+
+
+def route(q: np.ndarray, k: np.ndarray, block_q: int, block_k: int, p: float,
+          diagnostics: bool = False):
+    """q, k [B, H, N, d] -> dict(row_ptr, col_idx, head_load, nnz[, per-head diagnostics])."""
+    B, H, N, d = q.shape
+    kept_all, diags = [], []
+    for b in range(B):
+        for h in range(H):
+            kept, extra = route_head(q[b, h], k[b, h], block_q, block_k, p, diagnostics)
+            kept_all.append(kept)
+            diags.append(extra)
+    row_ptr, col_idx, head_load = csr_rows(kept_all)
+    out = dict(row_ptr=row_ptr, col_idx=col_idx, head_load=head_load, nnz=int(row_ptr[-1]),
+               kept=kept_all)
+    if diagnostics:
+        out["diag"] = diags
+    return out
+
+
+# --------------------------------------------------------------------------
+# Step 8: exact softmax attention over the kept blocks ([FVAttn]: attention then
+# runs only over the selected blocks; the sparse computation itself is exact).
+# Two-pass softmax (max, then exp and sum), scale 1/sqrt(d), fp64.
+# --------------------------------------------------------------------------
+def _attend(q_rows: np.ndarray, keys: np.ndarray, vals: np.ndarray) -> np.ndarray:
+    d = q_rows.shape[1]
+    s = (q_rows @ keys.T) / math.sqrt(d)
+    m = s.max(axis=1, keepdims=True)
+    w = np.exp(s - m)
+    return (w @ vals) / w.sum(axis=1, keepdims=True)
+
+
+def sparse_attention_rows(q_h, k_h, v_h, block_q: int, block_k: int,
+                          kept_rows: dict) -> dict:
+    """For one head: {query block i: o [len(block i), d]} for the rows in kept_rows
+    (i -> ascending kept key-block indices)."""
+    q_h = np.asarray(q_h, dtype=np.float64)
+    k_h = np.asarray(k_h, dtype=np.float64)
+    v_h = np.asarray(v_h, dtype=np.float64)
+    N = q_h.shape[0]
+    qb = block_bounds(N, block_q)
+    kb = block_bounds(N, block_k)
+    out = {}
+    for i, kept in kept_rows.items():
+        s0, e0 = qb[i]
+        tok = np.concatenate([np.arange(*kb[j]) for j in kept])
+        out[i] = _attend(q_h[s0:e0], k_h[tok], v_h[tok])
+    return out
+
+
+def sparse_attention(q, k, v, row_ptr, col_idx, block_q: int, block_k: int) -> np.ndarray:
+    """Full output o [B, H, N, d] (fp64) of block-sparse attention given a CSR over
+    rows r = (b*H + h) * nqb + i."""
+    B, H, N, d = q.shape
+    nqb = -(-N // block_q)
+    o = np.zeros((B, H, N, d), dtype=np.float64)
+    qb = block_bounds(N, block_q)
+    for b in range(B):
+        for h in range(H):
+            r0 = (b * H + h) * nqb
+            rows = {i: np.asarray(col_idx[row_ptr[r0 + i]:row_ptr[r0 + i + 1]]) for i in range(nqb)}
+            res = sparse_attention_rows(q[b, h], k[b, h], v[b, h], block_q, block_k, rows)
+            for i, oi in res.items():
+                o[b, h, qb[i][0]:qb[i][1]] = oi
+    return o
+
+
+def dense_attention(q, k, v) -> np.ndarray:
+    """Textbook softmax(q k^T / sqrt(d)) v per (b, h), fp64."""
+    B, H, N, d = q.shape
+    o = np.zeros((B, H, N, d), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            o[b, h] = _attend(np.asarray(q[b, h], np.float64), np.asarray(k[b, h], np.float64),
+                              np.asarray(v[b, h], np.float64))
+    return o
+
+
+# --------------------------------------------------------------------------
+# Step 7: one-GPU analogue of the runtime load balancing ([FVAttn] RLB section:
+# the heaviest work is moved first).  Tiles (rows) ordered by kept-block count,
+# longest first; equal counts keep ascending row id.
+# --------------------------------------------------------------------------
+def lpt_worklist(row_ptr: np.ndarray) -> np.ndarray:
+    counts = np.diff(np.asarray(row_ptr, dtype=np.int64))
+    return np.argsort(-counts, kind="stable").astype(np.int64)
