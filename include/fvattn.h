@@ -1,0 +1,193 @@
+/*
+ * fvattn.h - C ABI of the Top-p block-sparse attention library for MI355X (gfx950).
+ *
+ * Method (FVAttn, PaperDaily summary "腾讯+中山大学新作：视频生成提速2.11×，靠的是RLB和SASA",
+ * section "AI视频生成的阿喀琉斯之踵", Top-p routing paragraph): keys/values are cut into
+ * fixed blocks; for each query block every key block gets an importance, blocks are ranked
+ * in descending importance and the smallest prefix whose cumulative importance reaches p
+ * is kept; softmax attention then runs over the kept blocks only.  Block importance uses
+ * mean-pooled Q and K with a 1/sqrt(d) scale (tutorial page, section 5.2) followed by a
+ * softmax over key blocks; ties in importance go to the lower block index.
+ *
+ * Conventions shared by every entry point
+ *  - Tensors q, k, v, o are device pointers to contiguous [B, H, N, d] arrays (row-major,
+ *    d fastest), the layout of the tutorial's block-sparse function (section 5.2).
+ *  - Element type: FVATTN_BF16 (bfloat16; outputs rounded to nearest even) or FVATTN_F32.
+ *  - Supported: d in {64, 128}; block_q in {32, 64, 128}; block_k in {32, 64};
+ *    ceil(N / block_k) <= 1280.  Other values return FVATTN_ERR_UNSUPPORTED.
+ *  - Row r of the routing is (b*H + h) * nqb + i for query block i; nqb = ceil(N/block_q),
+ *    nkb = ceil(N/block_k).  The last block of each kind may be short (ragged): pooling
+ *    averages its real tokens only, and padding never attends or is attended to.
+ *  - Ownership: the caller owns every buffer, including workspaces; the library never
+ *    allocates device memory and keeps no state between calls.
+ *  - Asynchrony: compute calls validate their arguments on the host, enqueue kernels on
+ *    `stream` (a hipStream_t; NULL = the default stream) and return without synchronising.
+ *    Device outputs are valid once the stream has completed the work.
+ *  - Errors: a validation failure returns its code before anything is enqueued; a failed
+ *    launch returns FVATTN_ERR_HIP.  No C++ exception crosses the ABI.
+ */
+#ifndef FVATTN_H
+#define FVATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FVATTN_VERSION 10000 /* 1.0.0 */
+
+typedef enum fvattn_dtype { FVATTN_BF16 = 0, FVATTN_F32 = 1 } fvattn_dtype;
+
+enum {
+  FVATTN_OK = 0,
+  FVATTN_ERR_INVALID = -1,     /* bad value: p outside (0,1] or NaN, B/H/N <= 0, NULL pointer */
+  FVATTN_ERR_UNSUPPORTED = -2, /* d, block sizes, dtype or nkb outside the supported set     */
+  FVATTN_ERR_CAPACITY = -3,    /* csr->capacity < fvattn_csr_max_nnz(...)                     */
+  FVATTN_ERR_WORKSPACE = -4,   /* ws_bytes smaller than the matching *_ws_bytes() size        */
+  FVATTN_ERR_OVERFLOW = -5,    /* B*H*nqb*nkb does not fit in int32                            */
+  FVATTN_ERR_HIP = -6,         /* a HIP launch failed                                         */
+  FVATTN_ERR_MISMATCH = -7     /* CSR shape fields do not match the attention arguments       */
+};
+
+/* Work-list orders for fvattn_worklist / fvattn_sparse_attn. */
+enum {
+  FVATTN_SCHED_LPT = 0,      /* rows by kept-block count, longest first, ties by row id    */
+  FVATTN_SCHED_IDENTITY = 1, /* rows in ascending id (head-major) order                     */
+  FVATTN_SCHED_HEAD_LPT = 2  /* heads by load (heaviest first), rows of a head longest first */
+};
+
+/*
+ * Kept-block lists in CSR form, one row per (batch, head, query block).
+ * All pointers are device memory allocated by the caller.  fvattn_route fills the shape
+ * fields and the three arrays; fvattn_sparse_attn reads them and trusts the contents
+ * (col_idx values in [0, nkb), ascending, row_ptr non-decreasing), so a CSR built by
+ * other means (for example by a reference implementation) can be passed in.
+ * nnz = row_ptr[rows].  head_load[bh] = number of kept (query block, key block) pairs of
+ * that head: the per-head load of the FVAttn summary's RLB section (blocks a head must
+ * compute, read off its sparse mask).
+ */
+typedef struct fvattn_csr {
+  int32_t bh;        /* B*H                                             */
+  int32_t n;         /* tokens per head                                 */
+  int32_t block_q;   /* query block size                                */
+  int32_t block_k;   /* key block size                                  */
+  int32_t nqb;       /* ceil(n / block_q)                               */
+  int32_t nkb;       /* ceil(n / block_k)                               */
+  int32_t *row_ptr;  /* [bh*nqb + 1]                                    */
+  int32_t *col_idx;  /* [capacity]; per row ascending key-block ids     */
+  int64_t capacity;  /* elements available in col_idx                   */
+  int32_t *head_load;/* [bh]                                            */
+} fvattn_csr;
+
+/*
+ * Options of fvattn_sparse_attn; pass NULL for the defaults (LPT order, library grid,
+ * no trace).
+ *   schedule  one of FVATTN_SCHED_*.
+ *   grid      number of persistent workgroups; 0 = as many as stay resident.
+ *   trace     optional device array [rows * 4] of uint64: for each processed tile
+ *             {hardware id (XCC_ID << 32 | HW_ID), start clock, end clock, row}, clocks from
+ *             the 100 MHz constant-rate counter.  Used to measure per-CU busy time; costs a
+ *             few stores per tile.
+ *   out_dtype element type of o: -1 = the input dtype; FVATTN_F32 = float32 output (the
+ *             accumulator precision) for bf16 inputs.  With a bf16 output each value is the
+ *             round-to-nearest-even of the float32 result.
+ */
+typedef struct fvattn_attn_opts {
+  int32_t schedule;
+  int32_t grid;
+  uint64_t *trace;
+  int32_t out_dtype;
+  int32_t reserved;
+} fvattn_attn_opts;
+
+/* Library version (FVATTN_VERSION of the build). */
+int fvattn_version(void);
+
+/* Static string describing an error code. */
+const char *fvattn_strerror(int code);
+
+/* Worst-case CSR size B*H*nqb*nkb (every block kept), or a negative error code. */
+int64_t fvattn_csr_max_nnz(int B, int H, int N, int block_q, int block_k);
+
+/* Bytes of workspace fvattn_route needs (0 on invalid arguments). */
+size_t fvattn_route_ws_bytes(int B, int H, int N, int d, int block_q, int block_k);
+
+/* Bytes of workspace fvattn_sparse_attn needs (0 on invalid arguments). */
+size_t fvattn_attn_ws_bytes(int B, int H, int N, int d, int dtype, int block_q, int block_k);
+
+/*
+ * Block mean-pooling (tutorial page, section 5.2: a block is summarised by the mean of its
+ * tokens).  x: device [BH, N, d] of dtype; out: device float64 [BH, ceil(N/block), d], the
+ * mean over each block's real tokens accumulated in float64.  This is the first step of
+ * fvattn_route, exposed on its own.
+ */
+int fvattn_pool(const void *x, int BH, int N, int d, int dtype, int block, double *out,
+                void *stream);
+
+/*
+ * Top-p routing (FVAttn summary, Top-p routing paragraph): pooled scores
+ * s_ij = qbar_i . kbar_j / sqrt(d) (tutorial section 5.2), importance P_ij = softmax_j(s_ij),
+ * descending order with ties to the lower index, kept set = shortest prefix whose
+ * cumulative importance is >= p (p >= 1 keeps every block).  Scores, softmax and the cut
+ * are evaluated in float64 (cumulative mass as exact 2^-52 fixed point).
+ *   q, k       device [B, H, N, d] of dtype
+ *   p          in (0, 1]
+ *   csr        caller-filled pointers and capacity; shape fields are written
+ *   ws         device workspace of at least fvattn_route_ws_bytes(...) bytes
+ */
+int fvattn_route(const void *q, const void *k, int B, int H, int N, int d, int dtype,
+                 int block_q, int block_k, double p, fvattn_csr *csr, void *ws,
+                 size_t ws_bytes, void *stream);
+
+/*
+ * Device-built work list (one-GPU analogue of the FVAttn summary's runtime load balancing:
+ * the heaviest work is placed first).  worklist: device int32 [rows] receives a permutation
+ * of the rows in the requested FVATTN_SCHED_* order.  counter (optional, may be NULL):
+ * device int32[2] set to {0, 0} for a persistent consumer (tile ticket, exit count).
+ */
+int fvattn_worklist(const fvattn_csr *csr, int schedule, int32_t *worklist, int32_t *counter,
+                    void *stream);
+
+/*
+ * Block-sparse attention (FVAttn summary: attention runs only over the kept blocks; the
+ * sparse computation itself is exact): for each token t of query block i,
+ *   o_t = sum_{s in T(i)} softmax_s(q_t . k_s / sqrt(d)) v_s,
+ * T(i) = the real tokens of the key blocks listed in CSR row i.  bf16 inputs run on bf16
+ * MFMA with float32 accumulation and online softmax (P rounded to bf16 for P.V); float32
+ * inputs keep every step in float32.  Every row must list at least one block.
+ *   q, k, v    device [B, H, N, d] of dtype
+ *   o          device [B, H, N, d] of the output dtype (opts->out_dtype; default dtype),
+ *              written for every real token
+ *   csr        from fvattn_route or any valid CSR with matching shape fields
+ *   opts       may be NULL
+ *   ws         device workspace of at least fvattn_attn_ws_bytes(...) bytes
+ * Equivalent to fvattn_attn_plan(opts->schedule) followed by fvattn_attn_run.
+ */
+int fvattn_sparse_attn(const void *q, const void *k, const void *v, void *o, int B, int H,
+                       int N, int d, int dtype, const fvattn_csr *csr,
+                       const fvattn_attn_opts *opts, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * First half of fvattn_sparse_attn: builds the work list of the CSR rows in `schedule`
+ * order and, for bf16, the transposed copy of v the attention kernel stages from, all in
+ * `ws`.  The plan stays valid while v, the CSR and ws are unchanged.
+ */
+int fvattn_attn_plan(const void *v, int B, int H, int N, int d, int dtype, const fvattn_csr *csr,
+                     int schedule, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Second half of fvattn_sparse_attn: the attention kernel alone, consuming the plan held in
+ * `ws` (enqueue fvattn_attn_plan on the same workspace first, in stream order).  May be
+ * repeated on one plan; opts->schedule is ignored (the plan fixed the order).
+ */
+int fvattn_attn_run(const void *q, const void *k, const void *v, void *o, int B, int H, int N,
+                    int d, int dtype, const fvattn_csr *csr, const fvattn_attn_opts *opts,
+                    void *ws, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FVATTN_H */

@@ -1,0 +1,278 @@
+// extern "C" entry points of libfvattn: argument validation on the host (nothing is
+// enqueued unless every check passes), workspace carving, kernel launches.
+#include <math.h>
+#include <string.h>
+
+#include "common.h"
+
+namespace fv {
+int launch_pool(const void *x, int BH, int N, int d, int dtype, int block, int layout, double *out,
+                int32_t *zero_me, int nzero, hipStream_t st);
+int launch_select(const double *qsw, const double *ksw, int BH, int d, int nqb, int nkb, double p,
+                  int32_t *counts, uint32_t *bitmask, int nkw, int32_t *head_load, hipStream_t st);
+int launch_csr(const int32_t *counts, const uint32_t *bitmask, int rows, int nkw, int32_t *row_ptr,
+               int32_t *col_idx, hipStream_t st);
+int launch_vt(const void *v, void *vt, int BH, int N, int D, int NKP, hipStream_t st);
+int launch_worklist(const int32_t *row_ptr, int rows, int nqb, int nkb, int sched, int32_t *wl, int32_t *counter,
+                    hipStream_t st);
+int launch_attn_bf16(const void *q, const void *k, const void *vt, void *o, int out_f32, const int32_t *row_ptr,
+                     const int32_t *col_idx, const int32_t *wl, int32_t *counter, int rows, int nqb, int N, int NKP,
+                     int D, int BQ, int BK, int grid, uint64_t *trace, hipStream_t st);
+int launch_attn_f32(const void *q, const void *k, const void *v, void *o, const int32_t *row_ptr,
+                    const int32_t *col_idx, const int32_t *wl, int rows, int nqb, int N, int D, int BQ, int BK,
+                    uint64_t *trace, hipStream_t st);
+}  // namespace fv
+
+namespace {
+
+constexpr int kMaxNkb = 1280;
+constexpr int kMaxBH = 65535;
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Shape {
+  int B, H, N, d, bq, bk, BH, nqb, nkb, rows, nqbp, nkbp, nkw;
+};
+
+// Shape checks shared by every entry point.
+int check_shape(int B, int H, int N, int d, int bq, int bk, Shape *s) {
+  if (B <= 0 || H <= 0 || N <= 0) return FVATTN_ERR_INVALID;
+  if (d != 64 && d != 128) return FVATTN_ERR_UNSUPPORTED;
+  if (bq != 32 && bq != 64 && bq != 128) return FVATTN_ERR_UNSUPPORTED;
+  if (bk != 32 && bk != 64) return FVATTN_ERR_UNSUPPORTED;
+  const long long BH = (long long)B * H;
+  if (BH > kMaxBH) return FVATTN_ERR_OVERFLOW;
+  const long long nqb = (N + (long long)bq - 1) / bq, nkb = (N + (long long)bk - 1) / bk;
+  if (nkb > kMaxNkb) return FVATTN_ERR_UNSUPPORTED;
+  if (BH * nqb * nkb >= (1ll << 31)) return FVATTN_ERR_OVERFLOW;
+  if (BH * (long long)N * d >= (1ll << 40)) return FVATTN_ERR_OVERFLOW;
+  s->B = B; s->H = H; s->N = N; s->d = d; s->bq = bq; s->bk = bk;
+  s->BH = (int)BH; s->nqb = (int)nqb; s->nkb = (int)nkb; s->rows = (int)(BH * nqb);
+  s->nqbp = (int)((nqb + 15) / 16 * 16);
+  s->nkbp = (int)((nkb + 15) / 16 * 16);
+  s->nkw = (int)((nkb + 31) / 32);
+  return FVATTN_OK;
+}
+
+struct RouteWs {
+  double *qsw, *ksw;
+  int32_t *counts;
+  uint32_t *bitmask;
+  size_t bytes;
+};
+
+RouteWs route_ws_layout(const Shape &s, char *base) {
+  RouteWs w;
+  size_t off = 0;
+  w.qsw = (double *)(base + off);
+  off += align256((size_t)s.BH * s.nqbp * s.d * sizeof(double));
+  w.ksw = (double *)(base + off);
+  off += align256((size_t)s.BH * s.nkbp * s.d * sizeof(double));
+  w.counts = (int32_t *)(base + off);
+  off += align256((size_t)s.rows * sizeof(int32_t));
+  w.bitmask = (uint32_t *)(base + off);
+  off += align256((size_t)s.rows * s.nkw * sizeof(uint32_t));
+  w.bytes = off;
+  return w;
+}
+
+struct AttnWs {
+  int32_t *worklist, *counter;
+  uint16_t *vt;
+  int nkp;
+  size_t bytes;
+};
+
+AttnWs attn_ws_layout(const Shape &s, int dtype, char *base) {
+  AttnWs w;
+  size_t off = 0;
+  w.worklist = (int32_t *)(base + off);
+  off += align256((size_t)s.rows * sizeof(int32_t));
+  w.counter = (int32_t *)(base + off);
+  off += 256;
+  w.nkp = (s.N + 63) / 64 * 64;
+  w.vt = (uint16_t *)(base + off);
+  if (dtype == FVATTN_BF16) off += align256((size_t)s.BH * s.d * w.nkp * sizeof(uint16_t));
+  w.bytes = off;
+  return w;
+}
+
+bool dtype_ok(int dt) { return dt == FVATTN_BF16 || dt == FVATTN_F32; }
+
+}  // namespace
+
+extern "C" {
+
+int fvattn_version(void) { return FVATTN_VERSION; }
+
+const char *fvattn_strerror(int code) {
+  switch (code) {
+    case FVATTN_OK: return "ok";
+    case FVATTN_ERR_INVALID: return "invalid argument (p outside (0,1], non-positive size or NULL pointer)";
+    case FVATTN_ERR_UNSUPPORTED: return "unsupported head dim, block size, dtype or key-block count";
+    case FVATTN_ERR_CAPACITY: return "CSR capacity below the worst-case number of kept blocks";
+    case FVATTN_ERR_WORKSPACE: return "workspace smaller than required";
+    case FVATTN_ERR_OVERFLOW: return "problem size overflows 32-bit indexing";
+    case FVATTN_ERR_HIP: return "HIP launch failure";
+    case FVATTN_ERR_MISMATCH: return "CSR shape does not match the attention arguments";
+    default: return "unknown error code";
+  }
+}
+
+int64_t fvattn_csr_max_nnz(int B, int H, int N, int block_q, int block_k) {
+  Shape s;
+  const int rc = check_shape(B, H, N, 64, block_q, block_k, &s);
+  if (rc != FVATTN_OK) return rc;
+  return (int64_t)s.rows * s.nkb;
+}
+
+size_t fvattn_route_ws_bytes(int B, int H, int N, int d, int block_q, int block_k) {
+  Shape s;
+  if (check_shape(B, H, N, d, block_q, block_k, &s) != FVATTN_OK) return 0;
+  return route_ws_layout(s, nullptr).bytes;
+}
+
+size_t fvattn_attn_ws_bytes(int B, int H, int N, int d, int dtype, int block_q, int block_k) {
+  Shape s;
+  if (!dtype_ok(dtype) || check_shape(B, H, N, d, block_q, block_k, &s) != FVATTN_OK) return 0;
+  return attn_ws_layout(s, dtype, nullptr).bytes;
+}
+
+int fvattn_pool(const void *x, int BH, int N, int d, int dtype, int block, double *out, void *stream) {
+  if (!dtype_ok(dtype)) return FVATTN_ERR_UNSUPPORTED;
+  if (BH <= 0 || N <= 0) return FVATTN_ERR_INVALID;
+  if (d != 64 && d != 128) return FVATTN_ERR_UNSUPPORTED;
+  if (block != 32 && block != 64 && block != 128) return FVATTN_ERR_UNSUPPORTED;
+  if (BH > kMaxBH) return FVATTN_ERR_OVERFLOW;
+  if ((long long)BH * N * d >= (1ll << 40)) return FVATTN_ERR_OVERFLOW;
+  if (x == nullptr || out == nullptr) return FVATTN_ERR_INVALID;
+  return fv::launch_pool(x, BH, N, d, dtype, block, 0, out, nullptr, 0, (hipStream_t)stream);
+}
+
+int fvattn_route(const void *q, const void *k, int B, int H, int N, int d, int dtype, int block_q, int block_k,
+                 double p, fvattn_csr *csr, void *ws, size_t ws_bytes, void *stream) {
+  if (!dtype_ok(dtype)) return FVATTN_ERR_UNSUPPORTED;
+  Shape s;
+  int rc = check_shape(B, H, N, d, block_q, block_k, &s);
+  if (rc != FVATTN_OK) return rc;
+  if (!(p > 0.0 && p <= 1.0)) return FVATTN_ERR_INVALID;  // also rejects NaN
+  if (q == nullptr || k == nullptr || csr == nullptr || ws == nullptr) return FVATTN_ERR_INVALID;
+  if (csr->row_ptr == nullptr || csr->col_idx == nullptr || csr->head_load == nullptr) return FVATTN_ERR_INVALID;
+  if (csr->capacity < (int64_t)s.rows * s.nkb) return FVATTN_ERR_CAPACITY;
+  const RouteWs w = route_ws_layout(s, (char *)ws);
+  if (ws_bytes < w.bytes) return FVATTN_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+
+  csr->bh = s.BH; csr->n = N; csr->block_q = block_q; csr->block_k = block_k; csr->nqb = s.nqb; csr->nkb = s.nkb;
+  if ((rc = fv::launch_pool(q, s.BH, N, d, dtype, block_q, 1, w.qsw, nullptr, 0, st)) != FVATTN_OK) return rc;
+  if ((rc = fv::launch_pool(k, s.BH, N, d, dtype, block_k, 1, w.ksw, csr->head_load, s.BH, st)) != FVATTN_OK)
+    return rc;
+  if ((rc = fv::launch_select(w.qsw, w.ksw, s.BH, d, s.nqb, s.nkb, p, w.counts, w.bitmask, s.nkw, csr->head_load,
+                              st)) != FVATTN_OK)
+    return rc;
+  return fv::launch_csr(w.counts, w.bitmask, s.rows, s.nkw, csr->row_ptr, csr->col_idx, st);
+}
+
+int fvattn_worklist(const fvattn_csr *csr, int schedule, int32_t *worklist, int32_t *counter, void *stream) {
+  if (csr == nullptr || worklist == nullptr || csr->row_ptr == nullptr) return FVATTN_ERR_INVALID;
+  if (schedule != FVATTN_SCHED_LPT && schedule != FVATTN_SCHED_IDENTITY && schedule != FVATTN_SCHED_HEAD_LPT)
+    return FVATTN_ERR_INVALID;
+  if (csr->bh <= 0 || csr->nqb <= 0 || csr->nkb <= 0) return FVATTN_ERR_INVALID;
+  if (csr->nkb > kMaxNkb) return FVATTN_ERR_UNSUPPORTED;
+  if (schedule == FVATTN_SCHED_HEAD_LPT && csr->bh > 1024) return FVATTN_ERR_UNSUPPORTED;
+  if ((long long)csr->bh * csr->nqb >= (1ll << 31)) return FVATTN_ERR_OVERFLOW;
+  return fv::launch_worklist(csr->row_ptr, csr->bh * csr->nqb, csr->nqb, csr->nkb, schedule, worklist, counter,
+                             (hipStream_t)stream);
+}
+
+namespace {
+// Validation shared by plan / run / sparse_attn.  Returns the workspace layout through *w.
+int attn_checks(const void *v, int B, int H, int N, int d, int dtype, const fvattn_csr *csr, Shape *s, void *ws,
+                size_t ws_bytes, AttnWs *w) {
+  if (!dtype_ok(dtype)) return FVATTN_ERR_UNSUPPORTED;
+  if (csr == nullptr) return FVATTN_ERR_INVALID;
+  int rc = check_shape(B, H, N, d, csr->block_q, csr->block_k, s);
+  if (rc != FVATTN_OK) return rc;
+  if (v == nullptr || ws == nullptr) return FVATTN_ERR_INVALID;
+  if (csr->row_ptr == nullptr || csr->col_idx == nullptr) return FVATTN_ERR_INVALID;
+  if (csr->bh != s->BH || csr->n != N || csr->nqb != s->nqb || csr->nkb != s->nkb) return FVATTN_ERR_MISMATCH;
+  *w = attn_ws_layout(*s, dtype, (char *)ws);
+  if (ws_bytes < w->bytes) return FVATTN_ERR_WORKSPACE;
+  return FVATTN_OK;
+}
+
+int sched_ok(int sched, const Shape &s) {
+  if (sched != FVATTN_SCHED_LPT && sched != FVATTN_SCHED_IDENTITY && sched != FVATTN_SCHED_HEAD_LPT)
+    return FVATTN_ERR_INVALID;
+  if (sched == FVATTN_SCHED_HEAD_LPT && s.BH > 1024) return FVATTN_ERR_UNSUPPORTED;
+  return FVATTN_OK;
+}
+
+int run_checks(const void *q, const void *k, void *o, int dtype, const fvattn_attn_opts *opts, int *grid,
+               uint64_t **trace, int *out_dt) {
+  if (q == nullptr || k == nullptr || o == nullptr) return FVATTN_ERR_INVALID;
+  *grid = opts ? opts->grid : 0;
+  if (*grid < 0) return FVATTN_ERR_INVALID;
+  *trace = opts ? opts->trace : nullptr;
+  *out_dt = (opts && opts->out_dtype >= 0) ? opts->out_dtype : dtype;
+  if (!dtype_ok(*out_dt) || (dtype == FVATTN_F32 && *out_dt != FVATTN_F32)) return FVATTN_ERR_UNSUPPORTED;
+  return FVATTN_OK;
+}
+
+int do_plan(const void *v, const Shape &s, int dtype, const fvattn_csr *csr, int sched, const AttnWs &w,
+            hipStream_t st) {
+  int rc = fv::launch_worklist(csr->row_ptr, s.rows, s.nqb, s.nkb, sched, w.worklist, w.counter, st);
+  if (rc != FVATTN_OK || dtype == FVATTN_F32) return rc;
+  return fv::launch_vt(v, w.vt, s.BH, s.N, s.d, w.nkp, st);
+}
+
+int do_run(const void *q, const void *k, const void *v, void *o, const Shape &s, int dtype, int out_dt,
+           const fvattn_csr *csr, int grid, uint64_t *trace, const AttnWs &w, hipStream_t st) {
+  if (dtype == FVATTN_F32)
+    return fv::launch_attn_f32(q, k, v, o, csr->row_ptr, csr->col_idx, w.worklist, s.rows, s.nqb, s.N, s.d,
+                               csr->block_q, csr->block_k, trace, st);
+  return fv::launch_attn_bf16(q, k, w.vt, o, out_dt == FVATTN_F32, csr->row_ptr, csr->col_idx, w.worklist,
+                              w.counter, s.rows, s.nqb, s.N, w.nkp, s.d, csr->block_q, csr->block_k, grid, trace, st);
+}
+}  // namespace
+
+int fvattn_attn_plan(const void *v, int B, int H, int N, int d, int dtype, const fvattn_csr *csr, int schedule,
+                     void *ws, size_t ws_bytes, void *stream) {
+  Shape s;
+  AttnWs w;
+  int rc = attn_checks(v, B, H, N, d, dtype, csr, &s, ws, ws_bytes, &w);
+  if (rc != FVATTN_OK) return rc;
+  if ((rc = sched_ok(schedule, s)) != FVATTN_OK) return rc;
+  return do_plan(v, s, dtype, csr, schedule, w, (hipStream_t)stream);
+}
+
+int fvattn_attn_run(const void *q, const void *k, const void *v, void *o, int B, int H, int N, int d, int dtype,
+                    const fvattn_csr *csr, const fvattn_attn_opts *opts, void *ws, size_t ws_bytes, void *stream) {
+  Shape s;
+  AttnWs w;
+  int rc = attn_checks(v, B, H, N, d, dtype, csr, &s, ws, ws_bytes, &w);
+  if (rc != FVATTN_OK) return rc;
+  int grid, out_dt;
+  uint64_t *trace;
+  if ((rc = run_checks(q, k, o, dtype, opts, &grid, &trace, &out_dt)) != FVATTN_OK) return rc;
+  return do_run(q, k, v, o, s, dtype, out_dt, csr, grid, trace, w, (hipStream_t)stream);
+}
+
+int fvattn_sparse_attn(const void *q, const void *k, const void *v, void *o, int B, int H, int N, int d, int dtype,
+                       const fvattn_csr *csr, const fvattn_attn_opts *opts, void *ws, size_t ws_bytes,
+                       void *stream) {
+  Shape s;
+  AttnWs w;
+  int rc = attn_checks(v, B, H, N, d, dtype, csr, &s, ws, ws_bytes, &w);
+  if (rc != FVATTN_OK) return rc;
+  const int sched = opts ? opts->schedule : FVATTN_SCHED_LPT;
+  if ((rc = sched_ok(sched, s)) != FVATTN_OK) return rc;
+  int grid, out_dt;
+  uint64_t *trace;
+  if ((rc = run_checks(q, k, o, dtype, opts, &grid, &trace, &out_dt)) != FVATTN_OK) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  if ((rc = do_plan(v, s, dtype, csr, sched, w, st)) != FVATTN_OK) return rc;
+  return do_run(q, k, v, o, s, dtype, out_dt, csr, grid, trace, w, st);
+}
+
+}  // extern "C"

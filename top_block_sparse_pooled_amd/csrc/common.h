@@ -1,0 +1,57 @@
+// Shared definitions of the gfx950 kernels: vector types, bf16 conversions, launch checks.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fvattn.h"
+
+namespace fv {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef float f16v __attribute__((ext_vector_type(16)));
+typedef double d4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// bf16 bit pattern -> float (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// float -> bf16 bit pattern, round to nearest even (inputs are finite).
+__device__ __forceinline__ uint32_t f2bf(float x) {
+  uint32_t u = __float_as_uint(x);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  return f2bf(lo) | (f2bf(hi) << 16);
+}
+
+template <typename T> struct DT;
+template <> struct DT<uint16_t> { static constexpr int per16 = 8; };  // bf16 stored as u16
+template <> struct DT<float> { static constexpr int per16 = 4; };
+
+// Unpack one 16-byte chunk into float values.
+__device__ __forceinline__ void unpack16(const u32x4 &c, float *out, uint16_t) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = bf16_lo(c[i]);
+    out[2 * i + 1] = bf16_hi(c[i]);
+  }
+}
+__device__ __forceinline__ void unpack16(const u32x4 &c, float *out, float) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) out[i] = __uint_as_float(c[i]);
+}
+
+__host__ __device__ constexpr inline int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+}  // namespace fv
+
+// Returns FVATTN_ERR_HIP from the enclosing function if the last launch failed.
+#define FV_CHECK_LAUNCH()                                   \
+  do {                                                      \
+    if (hipGetLastError() != hipSuccess) return FVATTN_ERR_HIP; \
+  } while (0)
