@@ -203,22 +203,39 @@ __global__ __launch_bounds__(1024) void k_worklist(const int32_t *__restrict__ r
 // ---------------------------------------------------------------------------------------
 // bf16 MFMA attention.  Template: BQ query rows per tile (32/64/128), BK keys per block
 // (32/64), D head dim (64/128).
+//
+// LDS holds one K tile [BK][D] and one V^T tile [D][BK], filled straight from global memory
+// by global_load_lds_dwordx4 (no staging registers).  Each row of a tile is a run of 16-byte
+// chunks stored in XOR-swizzled order (chunk c of row r sits at position c ^ (r mod chunks)),
+// so the 16-byte operand reads of 16 consecutive rows hit distinct banks.  The two tiles are
+// refilled in a split pipeline with two barriers per key block:
+//    S = K_j Q^T | wait, barrier X | load K_{j+1} | softmax_j | O += V_j P | wait, barrier Y |
+//    load V_{j+1}
+// so K_{j+1} streams in behind the softmax and P.V of block j, and V_{j+1} behind S of j+1.
 // ---------------------------------------------------------------------------------------
 template <int BQ, int BK, int D>
 struct AttnCfg {
-  static constexpr int NW = BQ / 32;       // waves
+  static constexpr int NW = BQ / 32;       // waves, each owns 32 query rows
   static constexpr int NT = NW * 64;       // threads (= 2 * BQ)
-  static constexpr int KPAD = D + 8;       // K tile row stride (elements)
-  static constexpr int VPAD = BK + 8;      // V^T tile row stride (elements)
-  static constexpr int KCH = BK * D / 8;   // 16-byte chunks of a K tile
-  static constexpr int VCH = D * BK / 8;   // 16-byte chunks of a V^T tile
-  static constexpr int KPT = KCH / NT;     // chunks per thread
-  static constexpr int VPT = VCH / NT;
+  static constexpr int KROW = D * 2;       // bytes per K tile row (one key)
+  static constexpr int KCR = D / 8;        // 16-byte chunks per K row
+  static constexpr int VROW = BK * 2;      // bytes per V^T tile row (one dim)
+  static constexpr int VCR = BK / 8;       // chunks per V^T row
+  static constexpr int KBYTES = BK * D * 2;
+  static constexpr int VBYTES = D * BK * 2;
+  static constexpr int KI = KBYTES / 1024 / NW;  // 1 KB direct-to-LDS loads per wave
+  static constexpr int VI = VBYTES / 1024 / NW;
   static constexpr int NKT = BK / 32;      // 32-key tiles per block
   static constexpr int NS = D / 16;        // k-steps of S^T = K Q^T
   static constexpr int NM = D / 32;        // 32-dim tiles of O^T
-  static_assert(KCH % NT == 0 && VCH % NT == 0, "tile/thread mismatch");
+  static_assert(KBYTES % (1024 * NW) == 0 && VBYTES % (1024 * NW) == 0, "tile/wave mismatch");
 };
+
+typedef __attribute__((address_space(3))) void *lds_void_ptr;
+
+__device__ __forceinline__ void dma16(const void *src, void *lds_dst_uniform) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)lds_dst_uniform, 16, 0, 0);
+}
 
 __device__ __forceinline__ uint64_t hw_id_word() {
   const uint32_t hw = __builtin_amdgcn_s_getreg((31 << 11) | 4);    // HW_ID
@@ -227,18 +244,29 @@ __device__ __forceinline__ uint64_t hw_id_word() {
 }
 
 template <int BQ, int BK, int D>
-__global__ __launch_bounds__(2 * BQ) void k_attn_bf16(
+__global__ __launch_bounds__(2 * BQ, 2) void k_attn_bf16(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ vt,
     void *__restrict__ o, int out_f32, const int32_t *__restrict__ row_ptr, const int32_t *__restrict__ col_idx,
     const int32_t *__restrict__ worklist, int32_t *__restrict__ counter, int rows, int nqb, int N, int NKP,
     float sl2, uint64_t *__restrict__ trace) {
   using C = AttnCfg<BQ, BK, D>;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[BK * C::KPAD];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[D * C::VPAD];
+  __shared__ __attribute__((aligned(1024))) uint8_t Ks[C::KBYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t Vs[C::VBYTES];
   __shared__ int s_tile;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, kept in an SGPR
   const int l32 = lane & 31, h = lane >> 5;
+
+  // Swizzled positions.  The tile loads of one wave cover rows in groups (1 KB each);
+  // per lane the row inside the group and the chunk position are fixed, so only one row
+  // base and one XOR key are kept per lane and the rest is folded into constants.
+  constexpr int KRPI = 1024 / C::KROW;   // K rows per 1 KB load
+  constexpr int VRPI = 1024 / C::VROW;   // V^T rows per 1 KB load
+  const int k_r0 = lane / (C::KROW / 16), k_pos = lane % (C::KROW / 16);
+  const int v_r0 = lane / (C::VROW / 16), v_pos = lane % (C::VROW / 16);
+  // operand reads: row 32kt + l32 of K, row 32m + l32 of V^T; XOR keys depend only on l32
+  const int kx = l32 & (C::KCR - 1), vx = l32 & (C::VCR - 1);
 
   for (;;) {
     if (tid == 0) s_tile = atomicAdd(&counter[0], 1);
@@ -255,6 +283,29 @@ __global__ __launch_bounds__(2 * BQ) void k_attn_bf16(
     const uint16_t *kh = k + (size_t)bh * N * D;
     const uint16_t *vth = vt + (size_t)bh * D * NKP;
 
+    auto load_k = [&](int jb) {
+      const int key0 = jb * BK;
+#pragma unroll
+      for (int i = 0; i < C::KI; ++i) {
+        const int r = (w * C::KI + i) * KRPI + k_r0;          // tile row = key offset
+        const int key = min(key0 + r, N - 1);                // rows past N: any valid row, masked later
+        dma16(kh + (size_t)key * D + (k_pos ^ (r & (C::KCR - 1))) * 8, Ks + (w * C::KI + i) * 1024);
+      }
+    };
+    auto load_v = [&](int jb) {
+      const uint16_t *src = vth + jb * BK;
+#pragma unroll
+      for (int i = 0; i < C::VI; ++i) {
+        const int r = (w * C::VI + i) * VRPI + v_r0;          // tile row = head dim
+        dma16(src + (size_t)r * NKP + (v_pos ^ (r & (C::VCR - 1))) * 8, Vs + (w * C::VI + i) * 1024);
+      }
+    };
+
+    int jb = cnt > 0 ? col_idx[beg] : 0;
+    if (cnt > 0) {
+      load_k(jb);
+      load_v(jb);
+    }
     // Q fragments (operand B of S^T = K Q^T): query qrow, dims 16s + 8h .. +7
     const int qrow = qi * BQ + 32 * w + l32;
     bf16x8 qf[C::NS];
@@ -267,57 +318,18 @@ __global__ __launch_bounds__(2 * BQ) void k_attn_bf16(
         qf[s] = __builtin_bit_cast(bf16x8, raw);
       }
     }
-
     f16v oacc[C::NM];
 #pragma unroll
     for (int m = 0; m < C::NM; ++m)
 #pragma unroll
       for (int i = 0; i < 16; ++i) oacc[m][i] = 0.f;
-    float m_run = -INFINITY, l_run = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;   // m_run in log2 units (scores times sl2)
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
 
-    // register staging of the next block's tiles
-    u32x4 kreg[C::KPT], vreg[C::VPT];
-    auto load_tiles = [&](int jb) {
-      const int key0 = jb * BK;
-#pragma unroll
-      for (int i = 0; i < C::KPT; ++i) {
-        const int c = tid + i * C::NT;
-        const int r = c / (D / 8), cc = c % (D / 8);
-        const int key = key0 + r;
-        kreg[i] = u32x4{0u, 0u, 0u, 0u};
-        if (key < N) kreg[i] = *reinterpret_cast<const u32x4 *>(kh + (size_t)key * D + cc * 8);
-      }
-#pragma unroll
-      for (int i = 0; i < C::VPT; ++i) {
-        const int c = tid + i * C::NT;
-        const int r = c / (BK / 8), cc = c % (BK / 8);
-        vreg[i] = *reinterpret_cast<const u32x4 *>(vth + (size_t)r * NKP + key0 + cc * 8);
-      }
-    };
-    auto store_tiles = [&]() {
-#pragma unroll
-      for (int i = 0; i < C::KPT; ++i) {
-        const int c = tid + i * C::NT;
-        const int r = c / (D / 8), cc = c % (D / 8);
-        *reinterpret_cast<u32x4 *>(&Ks[r * C::KPAD + cc * 8]) = kreg[i];
-      }
-#pragma unroll
-      for (int i = 0; i < C::VPT; ++i) {
-        const int c = tid + i * C::NT;
-        const int r = c / (BK / 8), cc = c % (BK / 8);
-        *reinterpret_cast<u32x4 *>(&Vs[r * C::VPAD + cc * 8]) = vreg[i];
-      }
-    };
-
-    if (cnt > 0) load_tiles(col_idx[beg]);
     for (int jj = 0; jj < cnt; ++jj) {
-      const int jb = col_idx[beg + jj];
-      __syncthreads();  // previous block's LDS reads are done
-      store_tiles();
-      __syncthreads();
-      if (jj + 1 < cnt) load_tiles(col_idx[beg + jj + 1]);
-
-      // S^T tile(s): 32 keys x 32 queries each
+      const int jn = (jj + 1 < cnt) ? col_idx[beg + jj + 1] : 0;
+      // S^T tiles: 32 keys x 32 queries each
       f16v sacc[C::NKT];
 #pragma unroll
       for (int kt = 0; kt < C::NKT; ++kt) {
@@ -325,51 +337,64 @@ __global__ __launch_bounds__(2 * BQ) void k_attn_bf16(
         for (int i = 0; i < 16; ++i) sacc[kt][i] = 0.f;
 #pragma unroll
         for (int s = 0; s < C::NS; ++s) {
-          const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(&Ks[(32 * kt + l32) * C::KPAD + 16 * s + 8 * h]);
+          const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(
+              Ks + (32 * kt + l32) * C::KROW + (((2 * s + h) ^ kx) << 4));
           sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[s], sacc[kt], 0, 0, 0);
         }
       }
-      // online softmax (this lane: query l32 of wave w; keys 32kt + 8(v/4) + 4h + v%4)
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();                 // X: K tile free, V_j landed
+      if (jj + 1 < cnt) load_k(jn);
+
+      // online softmax (lane: query l32 of wave w; keys 32kt + 8(v/4) + 4h + v%4)
       const int kbase = jb * BK;
-      float mloc = -INFINITY;
+      if (kbase + BK > N) {            // ragged last block: mask keys >= N
+        const int lim = N - kbase - 4 * h;
+#pragma unroll
+        for (int kt = 0; kt < C::NKT; ++kt)
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            if (32 * kt + 8 * (v >> 2) + (v & 3) >= lim) sacc[kt][v] = -INFINITY;
+      }
+      float mloc = sacc[0][0];
 #pragma unroll
       for (int kt = 0; kt < C::NKT; ++kt)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int key = kbase + 32 * kt + 8 * (v >> 2) + 4 * h + (v & 3);
-          float x = sacc[kt][v] * sl2;
-          if (key >= N) x = -INFINITY;
-          sacc[kt][v] = x;
-          mloc = fmaxf(mloc, x);
-        }
+        for (int v = 0; v < 16; ++v) mloc = fmaxf(mloc, sacc[kt][v]);
       {
         auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mloc), __float_as_uint(mloc), false, false);
         mloc = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
       }
-      const float m_new = fmaxf(m_run, mloc);
-      const float alpha = exp2f(m_run - m_new);
-      m_run = m_new;
+      const float mb = mloc * sl2;
+      // rescale only when some row's maximum grew (wave-uniform branch); the largest
+      // weight of a row then stays exactly 1, so its bf16 copy carries no rounding error
+      if (__any(mb > m_run)) {
+        const float m_new = fmaxf(m_run, mb);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int m = 0; m < C::NM; ++m)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[m][i] *= alpha;
+      }
+      const float nm = -m_run;
       float psum = 0.f;
       bf16x8 pf[C::NKT][2];
 #pragma unroll
       for (int kt = 0; kt < C::NKT; ++kt)
 #pragma unroll
         for (int t2 = 0; t2 < 2; ++t2) {
-          uint32_t pk[4];
+          bf16x8 pv;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float p0 = exp2f(sacc[kt][8 * t2 + 2 * i] - m_new);
-            const float p1 = exp2f(sacc[kt][8 * t2 + 2 * i + 1] - m_new);
-            psum += p0 + p1;
-            pk[i] = pack_bf16(p0, p1);
+          for (int i = 0; i < 8; ++i) {
+            const float pe = __builtin_amdgcn_exp2f(fmaf(sacc[kt][8 * t2 + i], sl2, nm));
+            psum += pe;
+            pv[i] = (__bf16)pe;
           }
-          pf[kt][t2] = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
+          pf[kt][t2] = pv;
         }
-      l_run = l_run * alpha + psum;
-#pragma unroll
-      for (int m = 0; m < C::NM; ++m)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[m][i] *= alpha;
+      l_run += psum;
       // O^T += V^T P^T
 #pragma unroll
       for (int m = 0; m < C::NM; ++m)
@@ -377,12 +402,16 @@ __global__ __launch_bounds__(2 * BQ) void k_attn_bf16(
         for (int kt = 0; kt < C::NKT; ++kt)
 #pragma unroll
           for (int t2 = 0; t2 < 2; ++t2) {
-            const bf16x8 va =
-                *reinterpret_cast<const bf16x8 *>(&Vs[(32 * m + l32) * C::VPAD + 32 * kt + 16 * t2 + 8 * h]);
+            const bf16x8 va = *reinterpret_cast<const bf16x8 *>(
+                Vs + (32 * m + l32) * C::VROW + (((4 * kt + 2 * t2 + h) ^ vx) << 4));
             oacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[kt][t2], oacc[m], 0, 0, 0);
           }
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();                 // Y: V tile free, K_{j+1} landed
+      if (jj + 1 < cnt) load_v(jn);
+      jb = jn;
     }
-    // finalise: l over both halves, O / l, bf16, store (lane: query qrow, dims 32m+8a+4h+b)
+    // finalise: l over both halves, O / l, store (lane: query qrow, dims 32m + 8a + 4h + b)
     {
       auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
       const float ltot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
