@@ -45,6 +45,7 @@ def executed_flops(row_ptr, col_idx, N, nqb, block_q, block_k, d):
 def cu_balance(trace_np):
     """max/mean over CUs of busy time (union of the tile intervals run on each CU)."""
     import numpy as np
+    trace_np = trace_np[trace_np[:, 2] > 0]           # records that were written
     hw = trace_np[:, 0]
     key = ((hw >> 32) << 8) | ((hw >> 8) & 0xFF)       # (XCC id, SE/SH/CU id bits of HW_ID)
     t0, t1 = trace_np[:, 1].astype(np.int64), trace_np[:, 2].astype(np.int64)
@@ -111,7 +112,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="wan14b_n32760")
     ap.add_argument("--p", type=float, default=None)
-    ap.add_argument("--schedule", default="lpt", choices=["lpt", "identity", "head_lpt"])
+    ap.add_argument("--schedule", default="xcd", choices=["lpt", "identity", "head_lpt", "xcd"])
     ap.add_argument("--out", default="f32", choices=["f32", "bf16"],
                     help="output dtype of the attention (f32 = accumulator precision)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -202,7 +203,7 @@ def main():
     extras = {}
     if not args.no_extras:
         bal = {}
-        for sched in ("lpt", "identity", "head_lpt"):
+        for sched in ("lpt", "identity", "head_lpt", "xcd"):
             tr = torch.zeros(w.rows * 4, dtype=torch.int64, device=dev)
             fv.attn_plan(vd, csr, aws, sched)
             fv.attn_run(qd, kd, vd, csr, aws, out=o, out_dtype=out_dtype, trace=tr)

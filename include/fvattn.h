@@ -55,7 +55,10 @@ enum {
 enum {
   FVATTN_SCHED_LPT = 0,      /* rows by kept-block count, longest first, ties by row id    */
   FVATTN_SCHED_IDENTITY = 1, /* rows in ascending id (head-major) order                     */
-  FVATTN_SCHED_HEAD_LPT = 2  /* heads by load (heaviest first), rows of a head longest first */
+  FVATTN_SCHED_HEAD_LPT = 2, /* heads by load (heaviest first), rows of a head longest first */
+  FVATTN_SCHED_XCD = 3       /* rows in id order cut into 8 contiguous ranges of equal kept-block
+                                work, one per XCD (shared L2); an XCD that runs out takes rows
+                                from the others                                              */
 };
 
 /*
@@ -86,10 +89,12 @@ typedef struct fvattn_csr {
  * no trace).
  *   schedule  one of FVATTN_SCHED_*.
  *   grid      number of persistent workgroups; 0 = as many as stay resident.
- *   trace     optional device array [rows * 4] of uint64: for each processed tile
- *             {hardware id (XCC_ID << 32 | HW_ID), start clock, end clock, row}, clocks from
- *             the 100 MHz constant-rate counter.  Used to measure per-CU busy time; costs a
- *             few stores per tile.
+ *   trace     optional device array [rows * 4] of uint64.  Record t (t < units) describes the
+ *             t-th work unit taken: {hardware id (XCC_ID << 32 | HW_ID), start clock, end clock,
+ *             unit id}, clocks from the 100 MHz constant-rate counter.  A unit is 128/block_q
+ *             adjacent query blocks of one head for bf16 (128 query rows) and one query block for
+ *             float32; units = B*H*ceil(nqb/(128/block_q)) resp. B*H*nqb.  Records past `units`
+ *             are not written.  Used to measure per-CU busy time; costs a few stores per unit.
  *   out_dtype element type of o: -1 = the input dtype; FVATTN_F32 = float32 output (the
  *             accumulator precision) for bf16 inputs.  With a bf16 output each value is the
  *             round-to-nearest-even of the float32 result.
@@ -145,7 +150,8 @@ int fvattn_route(const void *q, const void *k, int B, int H, int N, int d, int d
  * Device-built work list (one-GPU analogue of the FVAttn summary's runtime load balancing:
  * the heaviest work is placed first).  worklist: device int32 [rows] receives a permutation
  * of the rows in the requested FVATTN_SCHED_* order.  counter (optional, may be NULL):
- * device int32[2] set to {0, 0} for a persistent consumer (tile ticket, exit count).
+ * device int32[64] control block of a persistent consumer (tickets, exit count and, for
+ * FVATTN_SCHED_XCD, the per-XCD row ranges), initialised by this call.
  */
 int fvattn_worklist(const fvattn_csr *csr, int schedule, int32_t *worklist, int32_t *counter,
                     void *stream);

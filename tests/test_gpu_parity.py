@@ -225,7 +225,7 @@ def test_determinism_schedule_independence_and_trace():
     csr = fv.route(qd, kd, 64, 64, 0.9)
     csr2 = fv.route(qd, kd, 64, 64, 0.9)
     assert torch.equal(csr.row_ptr, csr2.row_ptr) and torch.equal(csr.col_idx[: csr.nnz()], csr2.col_idx[: csr.nnz()])
-    outs = [fv.sparse_attn(qd, kd, vd, csr, schedule=s) for s in ("lpt", "lpt", "identity", "head_lpt")]
+    outs = [fv.sparse_attn(qd, kd, vd, csr, schedule=s) for s in ("lpt", "lpt", "identity", "head_lpt", "xcd")]
     outs.append(fv.sparse_attn(qd, kd, vd, csr, schedule="lpt", grid=7))
     for o in outs[1:]:
         assert torch.equal(outs[0], o)
@@ -233,12 +233,20 @@ def test_determinism_schedule_independence_and_trace():
     fv.attn_plan(vd, csr, ws, "lpt")
     for _ in range(3):   # the plan can be run repeatedly (the kernel resets its tile counter)
         assert torch.equal(fv.attn_run(qd, kd, vd, csr, ws), outs[0])
+    units = w.H * -(-w.nqb // 2)            # bf16 work units: pairs of 64-row query blocks
     trace = torch.zeros(w.rows * 4, dtype=torch.int64, device=DEV)
     o_t = fv.sparse_attn(qd, kd, vd, csr, trace=trace)
     assert torch.equal(o_t, outs[0])
     tr = trace.cpu().numpy().reshape(-1, 4).view(np.uint64)
-    assert sorted(tr[:, 3].astype(np.int64).tolist()) == list(range(w.rows))   # every tile exactly once
-    assert np.all(tr[:, 2] >= tr[:, 1])
+    assert sorted(tr[:units, 3].astype(np.int64).tolist()) == list(range(units))   # every unit exactly once
+    assert np.all(tr[:units, 2] >= tr[:units, 1]) and np.all(tr[units:] == 0)
+    # per-XCD queues with stealing: every tile exactly once, repeatable on one plan
+    fv.attn_plan(vd, csr, ws, "xcd")
+    for _ in range(3):
+        trace.zero_()
+        assert torch.equal(fv.attn_run(qd, kd, vd, csr, ws, trace=trace), outs[0])
+        tr = trace.cpu().numpy().reshape(-1, 4).view(np.uint64)
+        assert sorted(tr[:units, 3].astype(np.int64).tolist()) == list(range(units))
 
 
 # ------------------------------------------------------------------ full-size workloads

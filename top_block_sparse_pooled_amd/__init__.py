@@ -22,7 +22,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfvattn.so")
 
 BF16, F32 = 0, 1
-SCHED = {"lpt": 0, "identity": 1, "head_lpt": 2}
+SCHED = {"lpt": 0, "identity": 1, "head_lpt": 2, "xcd": 3}
 
 
 class FvAttnError(RuntimeError):
@@ -224,7 +224,7 @@ def worklist(csr: Csr, schedule: str = "lpt", with_counter: bool = False):
     """Device-built work list (permutation of the CSR rows) in the given order."""
     torch = _torch()
     wl = torch.empty(csr.rows, dtype=torch.int32, device=csr.row_ptr.device)
-    ctr = torch.empty(2, dtype=torch.int32, device=wl.device) if with_counter else None
+    ctr = torch.empty(64, dtype=torch.int32, device=wl.device) if with_counter else None
     c = csr.c()
     _check(lib().fvattn_worklist(ctypes.byref(c), SCHED[schedule], wl.data_ptr(),
                                  ctr.data_ptr() if ctr is not None else None, _stream(wl.device)),

@@ -13,8 +13,8 @@ int launch_select(const double *qsw, const double *ksw, int BH, int d, int nqb, 
 int launch_csr(const int32_t *counts, const uint32_t *bitmask, int rows, int nkw, int32_t *row_ptr,
                int32_t *col_idx, hipStream_t st);
 int launch_vt(const void *v, void *vt, int BH, int N, int D, int NKP, hipStream_t st);
-int launch_worklist(const int32_t *row_ptr, int rows, int nqb, int nkb, int sched, int32_t *wl, int32_t *counter,
-                    hipStream_t st);
+int launch_worklist(const int32_t *row_ptr, int rows, int nqb, int nkb, int G, int sched, int32_t *wl,
+                    int32_t *counter, hipStream_t st);
 int launch_attn_bf16(const void *q, const void *k, const void *vt, void *o, int out_f32, const int32_t *row_ptr,
                      const int32_t *col_idx, const int32_t *wl, int32_t *counter, int rows, int nqb, int N, int NKP,
                      int D, int BQ, int BK, int grid, uint64_t *trace, hipStream_t st);
@@ -175,13 +175,14 @@ int fvattn_route(const void *q, const void *k, int B, int H, int N, int d, int d
 
 int fvattn_worklist(const fvattn_csr *csr, int schedule, int32_t *worklist, int32_t *counter, void *stream) {
   if (csr == nullptr || worklist == nullptr || csr->row_ptr == nullptr) return FVATTN_ERR_INVALID;
-  if (schedule != FVATTN_SCHED_LPT && schedule != FVATTN_SCHED_IDENTITY && schedule != FVATTN_SCHED_HEAD_LPT)
+  if (schedule != FVATTN_SCHED_LPT && schedule != FVATTN_SCHED_IDENTITY && schedule != FVATTN_SCHED_HEAD_LPT &&
+      schedule != FVATTN_SCHED_XCD)
     return FVATTN_ERR_INVALID;
   if (csr->bh <= 0 || csr->nqb <= 0 || csr->nkb <= 0) return FVATTN_ERR_INVALID;
   if (csr->nkb > kMaxNkb) return FVATTN_ERR_UNSUPPORTED;
   if (schedule == FVATTN_SCHED_HEAD_LPT && csr->bh > 1024) return FVATTN_ERR_UNSUPPORTED;
   if ((long long)csr->bh * csr->nqb >= (1ll << 31)) return FVATTN_ERR_OVERFLOW;
-  return fv::launch_worklist(csr->row_ptr, csr->bh * csr->nqb, csr->nqb, csr->nkb, schedule, worklist, counter,
+  return fv::launch_worklist(csr->row_ptr, csr->bh * csr->nqb, csr->nqb, csr->nkb, 1, schedule, worklist, counter,
                              (hipStream_t)stream);
 }
 
@@ -202,7 +203,8 @@ int attn_checks(const void *v, int B, int H, int N, int d, int dtype, const fvat
 }
 
 int sched_ok(int sched, const Shape &s) {
-  if (sched != FVATTN_SCHED_LPT && sched != FVATTN_SCHED_IDENTITY && sched != FVATTN_SCHED_HEAD_LPT)
+  if (sched != FVATTN_SCHED_LPT && sched != FVATTN_SCHED_IDENTITY && sched != FVATTN_SCHED_HEAD_LPT &&
+      sched != FVATTN_SCHED_XCD)
     return FVATTN_ERR_INVALID;
   if (sched == FVATTN_SCHED_HEAD_LPT && s.BH > 1024) return FVATTN_ERR_UNSUPPORTED;
   return FVATTN_OK;
@@ -221,7 +223,9 @@ int run_checks(const void *q, const void *k, void *o, int dtype, const fvattn_at
 
 int do_plan(const void *v, const Shape &s, int dtype, const fvattn_csr *csr, int sched, const AttnWs &w,
             hipStream_t st) {
-  int rc = fv::launch_worklist(csr->row_ptr, s.rows, s.nqb, s.nkb, sched, w.worklist, w.counter, st);
+  // bf16 attention consumes units of 128 query rows (128 / block_q query blocks); fp32: rows
+  const int G = dtype == FVATTN_BF16 ? 128 / csr->block_q : 1;
+  int rc = fv::launch_worklist(csr->row_ptr, s.rows, s.nqb, s.nkb, G, sched, w.worklist, w.counter, st);
   if (rc != FVATTN_OK || dtype == FVATTN_F32) return rc;
   return fv::launch_vt(v, w.vt, s.BH, s.N, s.d, w.nkp, st);
 }

@@ -67,31 +67,47 @@ __global__ __launch_bounds__(256) void k_vt(const uint16_t *__restrict__ v, uint
 }
 
 // ---------------------------------------------------------------------------------------
-// k_worklist: permutation of the rows in the requested order.
-// single workgroup of 1024 threads (16 waves).
-//   LPT:      key = nkb - count (ascending key = descending count), stable in row id.
-//   HEAD_LPT: heads by load descending (ties: head id), then each head's rows as LPT.
+// k_worklist: permutation of the work units in the requested order.  A unit is G consecutive
+// query blocks of one head (G = 1: a CSR row); unit u = bh * ngroups + g covers rows
+// bh*nqb + g*G .. min(bh*nqb + g*G + G, (bh+1)*nqb) - 1, so its work (kept blocks) is one
+// difference of row_ptr.  Single workgroup of 1024 threads (16 waves).
+//   LPT:      key = nkb - ceil(work / G) (ascending key = heaviest first), stable in unit id.
+//   HEAD_LPT: heads by load descending (ties: head id), then each head's units as LPT.
+//   IDENTITY: unit id order.  XCD: unit id order cut into 8 ranges of equal work.
 // Stable counting sort: per-wave bin counts in LDS, bases by scan, then each wave scatters
-// its rows in 64-row chunks, ranking equal keys inside a chunk with bit-sliced ballots.
+// its units in 64-unit chunks, ranking equal keys inside a chunk with bit-sliced ballots.
 // ---------------------------------------------------------------------------------------
 constexpr int kWlWaves = 16;
 constexpr int kWlMaxBins = 1281 + 3;
 
-__device__ __forceinline__ int wl_key(const int32_t *row_ptr, int r, int nkb) {
-  int c = row_ptr[r + 1] - row_ptr[r];
-  c = c < 0 ? 0 : (c > nkb ? nkb : c);
-  return nkb - c;
-}
+struct UnitMap {
+  const int32_t *row_ptr;
+  int nqb, G, ngroups, nkb;
+  __device__ __forceinline__ int first_row(int u) const {
+    const int bh = u / ngroups, g = u - bh * ngroups;
+    return bh * nqb + g * G;
+  }
+  __device__ __forceinline__ int work(int u) const {
+    const int bh = u / ngroups, g = u - bh * ngroups;
+    const int r0 = bh * nqb + g * G, r1 = min(r0 + G, (bh + 1) * nqb);
+    return row_ptr[r1] - row_ptr[r0];
+  }
+  __device__ __forceinline__ int key(int u) const {
+    int c = (work(u) + G - 1) / G;
+    c = c < 0 ? 0 : (c > nkb ? nkb : c);
+    return nkb - c;
+  }
+};
 
-// Stable scatter of rows [lo, hi) of one wave by key, into out[] at positions given by the
+// Stable scatter of units [lo, hi) of one wave by key, into out[] at positions given by the
 // running per-key bases in bins[] (already offset).  Keys < 2048.
-__device__ void wl_scatter(const int32_t *row_ptr, int lo, int hi, int nkb, int *bins, int32_t *out) {
+__device__ void wl_scatter(const UnitMap &um, int lo, int hi, int *bins, int32_t *out) {
   const int lane = threadIdx.x & 63;
   const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int c0 = lo; c0 < hi; c0 += 64) {
-    const int r = c0 + lane;
-    const bool act = r < hi;
-    const int key = act ? wl_key(row_ptr, r, nkb) : 0;
+    const int u = c0 + lane;
+    const bool act = u < hi;
+    const int key = act ? um.key(u) : 0;
     unsigned long long peers = __ballot(act);
 #pragma unroll
     for (int b = 0; b < 11; ++b) {
@@ -104,7 +120,7 @@ __device__ void wl_scatter(const int32_t *row_ptr, int lo, int hi, int nkb, int 
     __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_wave_barrier();
     if (act) {
-      out[base + rank] = r;
+      out[base + rank] = u;
       if (rank == 0) bins[key] = base + __popcll(peers);
     }
     __builtin_amdgcn_wave_barrier();
@@ -112,27 +128,47 @@ __device__ void wl_scatter(const int32_t *row_ptr, int lo, int hi, int nkb, int 
 }
 
 __global__ __launch_bounds__(1024) void k_worklist(const int32_t *__restrict__ row_ptr, int rows, int nqb,
-                                                   int nkb, int sched, int32_t *__restrict__ wl,
+                                                   int nkb, int G, int sched, int32_t *__restrict__ wl,
                                                    int32_t *__restrict__ counter) {
   __shared__ int bins[kWlWaves][kWlMaxBins];
   __shared__ int s_scan[1024];
   __shared__ int s_hbase[1024];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int nh = rows / nqb;
+  const int ngroups = (nqb + G - 1) / G;
+  const int units = nh * ngroups;
+  const UnitMap um{row_ptr, nqb, G, ngroups, nkb};
+  // control block: [0] ticket, [1] exit count, [2] per-XCD mode, [8+x] XCD x ticket,
+  // [16+x] start of XCD x's unit range (x = 0..8, [24] = units)
   if (tid == 0 && counter != nullptr) {
-    counter[0] = 0;  // tile ticket
-    counter[1] = 0;  // workgroups that have finished
+    counter[0] = 0;
+    counter[1] = 0;
+    counter[2] = (sched == FVATTN_SCHED_XCD) ? 1 : 0;
   }
-  if (sched == FVATTN_SCHED_IDENTITY) {
-    for (int r = tid; r < rows; r += 1024) wl[r] = r;
+  if (sched == FVATTN_SCHED_IDENTITY || sched == FVATTN_SCHED_XCD) {
+    for (int u = tid; u < units; u += 1024) wl[u] = u;
+    if (sched == FVATTN_SCHED_XCD && counter != nullptr && tid < 9) {
+      // range x starts at the first unit whose kept blocks begin at or after x/8 of the total
+      const long long nnz = row_ptr[rows];
+      const long long target = nnz * tid / 8;
+      int lo = 0, hi = units;   // first unit u with row_ptr[first_row(u)] >= target
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (row_ptr[um.first_row(mid)] < target) lo = mid + 1; else hi = mid;
+      }
+      const int start = tid == 8 ? units : lo;
+      counter[16 + tid] = start;
+      if (tid < 8) counter[8 + tid] = start;
+    }
     return;
   }
   const int nbins = nkb + 1;
   if (sched == FVATTN_SCHED_LPT) {
     for (int i = tid; i < kWlWaves * kWlMaxBins; i += 1024) (&bins[0][0])[i] = 0;
     __syncthreads();
-    const int seg = cdiv(rows, kWlWaves);
-    const int lo = min(rows, w * seg), hi = min(rows, lo + seg);
-    for (int r = lo + lane; r < hi; r += 64) atomicAdd(&bins[w][wl_key(row_ptr, r, nkb)], 1);
+    const int seg = cdiv(units, kWlWaves);
+    const int lo = min(units, w * seg), hi = min(units, lo + seg);
+    for (int u = lo + lane; u < hi; u += 64) atomicAdd(&bins[w][um.key(u)], 1);
     __syncthreads();
     // totals per bin, exclusive scan over bins (two bins per thread)
     int t0 = 0, t1 = 0;
@@ -156,12 +192,10 @@ __global__ __launch_bounds__(1024) void k_worklist(const int32_t *__restrict__ r
       if (b1 < nbins) { const int c = bins[i][b1]; bins[i][b1] = run1; run1 += c; }
     }
     __syncthreads();
-    wl_scatter(row_ptr, lo, hi, nkb, bins[w], wl);
+    wl_scatter(um, lo, hi, bins[w], wl);
     return;
   }
-  // HEAD_LPT
-  const int nh = rows / nqb;
-  // rank heads by load (desc), ties by id; bases = prefix of ranked head sizes (all nqb)
+  // HEAD_LPT: rank heads by load (desc), ties by id; a head's units start at rank * ngroups
   for (int h = tid; h < nh; h += 1024) {
     const int lh = row_ptr[(h + 1) * nqb] - row_ptr[h * nqb];
     int rank = 0;
@@ -169,15 +203,15 @@ __global__ __launch_bounds__(1024) void k_worklist(const int32_t *__restrict__ r
       const int l2 = row_ptr[(h2 + 1) * nqb] - row_ptr[h2 * nqb];
       rank += (l2 > lh) || (l2 == lh && h2 < h);
     }
-    s_hbase[h] = rank * nqb;
+    s_hbase[h] = rank * ngroups;
   }
   __syncthreads();
   for (int h = w; h < nh; h += kWlWaves) {
     int *bw = bins[w];
     for (int i = lane; i < nbins; i += 64) bw[i] = 0;
     __builtin_amdgcn_wave_barrier();
-    const int lo = h * nqb, hi = lo + nqb;
-    for (int r = lo + lane; r < hi; r += 64) atomicAdd(&bw[wl_key(row_ptr, r, nkb)], 1);
+    const int lo = h * ngroups, hi = lo + ngroups;
+    for (int u = lo + lane; u < hi; u += 64) atomicAdd(&bw[um.key(u)], 1);
     __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_wave_barrier();
     // exclusive scan of the bins by this wave (chunks of 64)
@@ -196,27 +230,31 @@ __global__ __launch_bounds__(1024) void k_worklist(const int32_t *__restrict__ r
     }
     __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_wave_barrier();
-    wl_scatter(row_ptr, lo, hi, nkb, bw, wl);
+    wl_scatter(um, lo, hi, bw, wl);
   }
 }
 
 // ---------------------------------------------------------------------------------------
-// bf16 MFMA attention.  Template: BQ query rows per tile (32/64/128), BK keys per block
-// (32/64), D head dim (64/128).
+// bf16 MFMA attention.  Template: BQ query rows per query block (32/64/128), BK keys per key
+// block (32/64), D head dim (64/128).
 //
-// LDS holds one K tile [BK][D] and one V^T tile [D][BK], filled straight from global memory
-// by global_load_lds_dwordx4 (no staging registers).  Each row of a tile is a run of 16-byte
-// chunks stored in XOR-swizzled order (chunk c of row r sits at position c ^ (r mod chunks)),
-// so the 16-byte operand reads of 16 consecutive rows hit distinct banks.  The two tiles are
-// refilled in a split pipeline with two barriers per key block:
-//    S = K_j Q^T | wait, barrier X | load K_{j+1} | softmax_j | O += V_j P | wait, barrier Y |
-//    load V_{j+1}
-// so K_{j+1} streams in behind the softmax and P.V of block j, and V_{j+1} behind S of j+1.
+// A workgroup is 4 waves = 128 query rows = G = 128/BQ adjacent query blocks of one head (a
+// work unit); each wave owns 32 query rows of one of them.  The workgroup walks the union of
+// the G kept-block lists in ascending key order; each key block's K and V^T tiles are loaded
+// once into LDS and used by every wave whose query block kept it (adjacent query blocks of a
+// video layer keep largely the same blocks), the other waves skip it.
+//
+// LDS holds two K tiles [BK][D] and two V^T tiles [D][BK] filled straight from global memory
+// by buffer_load ... lds (no staging registers; per-head buffer resources make rows past N
+// read as zero).  Rows are runs of 16-byte chunks in XOR-swizzled order (rows that share a
+// 256-byte bank line get different XOR keys) so the 16-byte operand reads of 16 consecutive
+// rows hit distinct banks.  Tiles are double buffered: the next block's loads are issued
+// right after the one barrier per block and have a whole block of compute to land.
 // ---------------------------------------------------------------------------------------
-template <int BQ, int BK, int D>
+template <int BK, int D>
 struct AttnCfg {
-  static constexpr int NW = BQ / 32;       // waves, each owns 32 query rows
-  static constexpr int NT = NW * 64;       // threads (= 2 * BQ)
+  static constexpr int NW = 4;             // waves per workgroup
+  static constexpr int NT = NW * 64;
   static constexpr int KROW = D * 2;       // bytes per K tile row (one key)
   static constexpr int KCR = D / 8;        // 16-byte chunks per K row
   static constexpr int VROW = BK * 2;      // bytes per V^T tile row (one dim)
@@ -225,6 +263,15 @@ struct AttnCfg {
   static constexpr int VBYTES = D * BK * 2;
   static constexpr int KI = KBYTES / 1024 / NW;  // 1 KB direct-to-LDS loads per wave
   static constexpr int VI = VBYTES / 1024 / NW;
+  static constexpr int KRP = KROW >= 256 ? 1 : 256 / KROW;   // rows sharing one 256-byte bank line
+  static constexpr int VRP = VROW >= 256 ? 1 : 256 / VROW;
+  static constexpr int KRPI = 1024 / KROW; // rows per 1 KB load
+  static constexpr int VRPI = 1024 / VROW;
+  static constexpr int KPER = (KCR * KRP) / KRPI > 0 ? (KCR * KRP) / KRPI : 1;  // loads before the
+  static constexpr int VPER = (VCR * VRP) / VRPI > 0 ? (VCR * VRP) / VRPI : 1;  // swizzle repeats
+  static_assert(KPER * KRPI == KRP * KCR && VPER * VRPI == VRP * VCR, "swizzle period");
+  static constexpr bool KTAB = (KI % KPER) == 0;  // load i of every wave has swizzle phase i % KPER
+  static constexpr bool VTAB = (VI % VPER) == 0;
   static constexpr int NKT = BK / 32;      // 32-key tiles per block
   static constexpr int NS = D / 16;        // k-steps of S^T = K Q^T
   static constexpr int NM = D / 32;        // 32-dim tiles of O^T
@@ -233,8 +280,20 @@ struct AttnCfg {
 
 typedef __attribute__((address_space(3))) void *lds_void_ptr;
 
-__device__ __forceinline__ void dma16(const void *src, void *lds_dst_uniform) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)lds_dst_uniform, 16, 0, 0);
+// Raw buffer resource over `bytes` bytes at `base`: loads past the end return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// 16 bytes per lane from the buffer straight into LDS at lds_dst (wave-uniform) + 16 * lane.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void *lds_dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_ptr)lds_dst, 16, voff, soff, 0, 0);
+}
+
+// 16-byte chunk position of chunk c in row r of a swizzled tile (rows of `rowbytes` bytes,
+// `cr` chunks per row): rows that share a 256-byte bank line get different XOR keys.
+__host__ __device__ constexpr int swz_pos(int c, int r, int rowbytes, int cr) {
+  return c ^ ((r / (rowbytes >= 256 ? 1 : 256 / rowbytes)) & (cr - 1));
 }
 
 __device__ __forceinline__ uint64_t hw_id_word() {
@@ -244,77 +303,148 @@ __device__ __forceinline__ uint64_t hw_id_word() {
 }
 
 template <int BQ, int BK, int D>
-__global__ __launch_bounds__(2 * BQ, 2) void k_attn_bf16(
+__global__ __launch_bounds__(256, 2) void k_attn_bf16(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ vt,
     void *__restrict__ o, int out_f32, const int32_t *__restrict__ row_ptr, const int32_t *__restrict__ col_idx,
-    const int32_t *__restrict__ worklist, int32_t *__restrict__ counter, int rows, int nqb, int N, int NKP,
-    float sl2, uint64_t *__restrict__ trace) {
-  using C = AttnCfg<BQ, BK, D>;
-  __shared__ __attribute__((aligned(1024))) uint8_t Ks[C::KBYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t Vs[C::VBYTES];
+    const int32_t *__restrict__ worklist, int32_t *__restrict__ counter, int units, int ngroups, int nqb, int N,
+    int NKP, float sl2, uint64_t *__restrict__ trace) {
+  using C = AttnCfg<BK, D>;
+  constexpr int G = 128 / BQ;     // query blocks per unit
+  constexpr int WPQ = BQ / 32;    // waves per query block
+  constexpr int NONE = 0x7fffffff;
+  __shared__ __attribute__((aligned(1024))) uint8_t Ks[2 * C::KBYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t Vs[2 * C::VBYTES];
   __shared__ int s_tile;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, kept in an SGPR
+  const int wq = w / WPQ, wr = w % WPQ;                     // query block of the unit, 32-row slice
   const int l32 = lane & 31, h = lane >> 5;
 
-  // Swizzled positions.  The tile loads of one wave cover rows in groups (1 KB each);
-  // per lane the row inside the group and the chunk position are fixed, so only one row
-  // base and one XOR key are kept per lane and the rest is folded into constants.
-  constexpr int KRPI = 1024 / C::KROW;   // K rows per 1 KB load
-  constexpr int VRPI = 1024 / C::VROW;   // V^T rows per 1 KB load
-  const int k_r0 = lane / (C::KROW / 16), k_pos = lane % (C::KROW / 16);
-  const int v_r0 = lane / (C::VROW / 16), v_pos = lane % (C::VROW / 16);
-  // operand reads: row 32kt + l32 of K, row 32m + l32 of V^T; XOR keys depend only on l32
-  const int kx = l32 & (C::KCR - 1), vx = l32 & (C::VCR - 1);
+  // Tile loads: load i of wave w fills LDS bytes [(w*KI + i) KB, +1 KB) of a tile; lane L writes
+  // the 16 bytes at +16 L, i.e. tile row (w*KI + i)*KRPI + L/(row chunks), position
+  // L%(row chunks), and fetches the chunk whose swizzled position that is.  The swizzle repeats
+  // every KPER (VPER) loads, so a handful of per-lane offsets cover all loads.
+  const int k_r0 = lane / C::KCR, k_pos = lane % C::KCR;
+  const int v_r0 = lane / C::VCR, v_pos = lane % C::VCR;
+  uint32_t k_vo[C::KPER], v_vo[C::VPER];
+#pragma unroll
+  for (int j = 0; j < C::KPER; ++j) {
+    const int r = j * C::KRPI + k_r0;
+    k_vo[j] = (uint32_t)(k_r0 * C::KROW + swz_pos(k_pos, r, C::KROW, C::KCR) * 16);
+  }
+#pragma unroll
+  for (int j = 0; j < C::VPER; ++j) {
+    const int r = j * C::VRPI + v_r0;
+    v_vo[j] = (uint32_t)(v_r0 * NKP * 2 + swz_pos(v_pos, r, C::VROW, C::VCR) * 16);
+  }
 
+  const bool per_xcd = counter[2] != 0;
+  const int xcc = (int)(__builtin_amdgcn_s_getreg((31 << 11) | 20) & 7);   // XCC_ID
   for (;;) {
-    if (tid == 0) s_tile = atomicAdd(&counter[0], 1);
+    if (tid == 0) {
+      int tk = units;
+      if (!per_xcd) {
+        tk = atomicAdd(&counter[0], 1);
+      } else {
+        for (int qq = 0; qq < 8; ++qq) {     // own XCD's range first, then the others'
+          const int x = (xcc + qq) & 7;
+          const int c = atomicAdd(&counter[8 + x], 1);
+          if (c < counter[17 + x]) {
+            tk = c;
+            break;
+          }
+        }
+      }
+      s_tile = tk;
+    }
     __syncthreads();
     const int t = s_tile;
     __syncthreads();
-    if (t >= rows) break;
+    if (t >= units) break;
     uint64_t t_start = 0;
     if (trace != nullptr) t_start = __builtin_amdgcn_s_memrealtime();
 
-    const int row = worklist[t];
-    const int bh = row / nqb, qi = row - bh * nqb;
-    const int beg = row_ptr[row], cnt = row_ptr[row + 1] - beg;
+    const int u = worklist[t];
+    const int bh = u / ngroups, g = u - bh * ngroups;
+    const int r0 = bh * nqb + g * G;                // first CSR row of the unit
+    const int nrow = min(G, nqb - g * G);           // query blocks present in the unit
     const uint16_t *kh = k + (size_t)bh * N * D;
     const uint16_t *vth = vt + (size_t)bh * D * NKP;
-
-    auto load_k = [&](int jb) {
-      const int key0 = jb * BK;
+    const __amdgpu_buffer_rsrc_t krs = buf_rsrc(kh, (uint32_t)N * D * 2);
+    const __amdgpu_buffer_rsrc_t vrs = buf_rsrc(vth, (uint32_t)D * NKP * 2);
+    auto load_k = [&](int jb, int buf) {
+      const uint32_t sbase = (uint32_t)jb * BK * D * 2 + (uint32_t)w * C::KI * C::KRPI * C::KROW;
+      uint8_t *dst = Ks + buf * C::KBYTES + w * C::KI * 1024;
 #pragma unroll
       for (int i = 0; i < C::KI; ++i) {
-        const int r = (w * C::KI + i) * KRPI + k_r0;          // tile row = key offset
-        const int key = min(key0 + r, N - 1);                // rows past N: any valid row, masked later
-        dma16(kh + (size_t)key * D + (k_pos ^ (r & (C::KCR - 1))) * 8, Ks + (w * C::KI + i) * 1024);
+        uint32_t vo;
+        if constexpr (C::KTAB) {
+          vo = k_vo[i % C::KPER];
+        } else {
+          const int gi = w * C::KI + i;
+          vo = (uint32_t)(k_r0 * C::KROW + swz_pos(k_pos, gi * C::KRPI + k_r0, C::KROW, C::KCR) * 16);
+        }
+        dma16(krs, vo, sbase + (uint32_t)i * C::KRPI * C::KROW, dst + i * 1024);
       }
     };
-    auto load_v = [&](int jb) {
-      const uint16_t *src = vth + jb * BK;
+    auto load_v = [&](int jb, int buf) {
+      const uint32_t sbase = (uint32_t)jb * BK * 2 + (uint32_t)w * C::VI * C::VRPI * NKP * 2;
+      uint8_t *dst = Vs + buf * C::VBYTES + w * C::VI * 1024;
 #pragma unroll
       for (int i = 0; i < C::VI; ++i) {
-        const int r = (w * C::VI + i) * VRPI + v_r0;          // tile row = head dim
-        dma16(src + (size_t)r * NKP + (v_pos ^ (r & (C::VCR - 1))) * 8, Vs + (w * C::VI + i) * 1024);
+        uint32_t vo;
+        if constexpr (C::VTAB) {
+          vo = v_vo[i % C::VPER];
+        } else {
+          const int gi = w * C::VI + i;
+          vo = (uint32_t)(v_r0 * NKP * 2 + swz_pos(v_pos, gi * C::VRPI + v_r0, C::VROW, C::VCR) * 16);
+        }
+        dma16(vrs, vo, sbase + (uint32_t)i * C::VRPI * NKP * 2, dst + i * 1024);
       }
     };
 
-    int jb = cnt > 0 ? col_idx[beg] : 0;
-    if (cnt > 0) {
-      load_k(jb);
-      load_v(jb);
+    // merge of the unit's G ascending kept lists (identical in every thread)
+    int ptr[G], endp[G], hd[G];
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) {
+      ptr[gi] = gi < nrow ? row_ptr[r0 + gi] : 0;
+      endp[gi] = gi < nrow ? row_ptr[r0 + gi + 1] : 0;
+      hd[gi] = ptr[gi] < endp[gi] ? col_idx[ptr[gi]] : NONE;
     }
-    // Q fragments (operand B of S^T = K Q^T): query qrow, dims 16s + 8h .. +7
-    const int qrow = qi * BQ + 32 * w + l32;
+    auto advance = [&](int &jb, int &mask) {
+      jb = NONE;
+#pragma unroll
+      for (int gi = 0; gi < G; ++gi) jb = min(jb, hd[gi]);
+      mask = 0;
+      if (jb == NONE) return;
+#pragma unroll
+      for (int gi = 0; gi < G; ++gi)
+        if (hd[gi] == jb) {
+          mask |= 1 << gi;
+          ++ptr[gi];
+          hd[gi] = ptr[gi] < endp[gi] ? col_idx[ptr[gi]] : NONE;
+        }
+    };
+    int cur_j, cur_m, nxt_j, nxt_m;
+    advance(cur_j, cur_m);
+    advance(nxt_j, nxt_m);
+    if (cur_j != NONE) {
+      load_k(cur_j, 0);
+      load_v(cur_j, 0);
+    }
+
+    // this wave's query rows
+    const int qi = g * G + wq;
+    const int qrow = qi * BQ + 32 * wr + l32;
+    const bool qlive = qi < nqb && qrow < N;
     bf16x8 qf[C::NS];
     {
-      const uint16_t *qp = q + ((size_t)bh * N + (qrow < N ? qrow : 0)) * D + 8 * h;
+      const uint16_t *qp = q + ((size_t)bh * N + (qlive ? qrow : 0)) * D + 8 * h;
 #pragma unroll
       for (int s = 0; s < C::NS; ++s) {
         u32x4 raw = {0u, 0u, 0u, 0u};
-        if (qrow < N) raw = *reinterpret_cast<const u32x4 *>(qp + 16 * s);
+        if (qlive) raw = *reinterpret_cast<const u32x4 *>(qp + 16 * s);
         qf[s] = __builtin_bit_cast(bf16x8, raw);
       }
     }
@@ -323,100 +453,104 @@ __global__ __launch_bounds__(2 * BQ, 2) void k_attn_bf16(
     for (int m = 0; m < C::NM; ++m)
 #pragma unroll
       for (int i = 0; i < 16; ++i) oacc[m][i] = 0.f;
-    float m_run = -INFINITY, l_run = 0.f;   // m_run in log2 units (scores times sl2)
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    float m_run = -INFINITY, l_run = 0.f;   // running row maximum (log2 units) and row sum
 
-    for (int jj = 0; jj < cnt; ++jj) {
-      const int jn = (jj + 1 < cnt) ? col_idx[beg + jj + 1] : 0;
-      // S^T tiles: 32 keys x 32 queries each
-      f16v sacc[C::NKT];
-#pragma unroll
-      for (int kt = 0; kt < C::NKT; ++kt) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[kt][i] = 0.f;
-#pragma unroll
-        for (int s = 0; s < C::NS; ++s) {
-          const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(
-              Ks + (32 * kt + l32) * C::KROW + (((2 * s + h) ^ kx) << 4));
-          sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[s], sacc[kt], 0, 0, 0);
-        }
-      }
+    for (int st = 0; cur_j != NONE; ++st) {
+      const int b = st & 1;
       __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();                 // X: K tile free, V_j landed
-      if (jj + 1 < cnt) load_k(jn);
-
-      // online softmax (lane: query l32 of wave w; keys 32kt + 8(v/4) + 4h + v%4)
-      const int kbase = jb * BK;
-      if (kbase + BK > N) {            // ragged last block: mask keys >= N
-        const int lim = N - kbase - 4 * h;
+      __syncthreads();                 // tiles of cur_j landed; buffer b^1 no longer read
+      if (nxt_j != NONE) {
+        load_k(nxt_j, b ^ 1);
+        load_v(nxt_j, b ^ 1);
+      }
+      if ((cur_m >> wq) & 1) {         // wave-uniform: this wave's query block kept cur_j
+        const uint8_t *kb = Ks + b * C::KBYTES;
+        const uint8_t *vb = Vs + b * C::VBYTES;
+        // S^T tiles: 32 keys x 32 queries each
+        f16v sacc[C::NKT];
+#pragma unroll
+        for (int kt = 0; kt < C::NKT; ++kt) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sacc[kt][i] = 0.f;
+#pragma unroll
+          for (int s = 0; s < C::NS; ++s) {
+            const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(
+                kb + (32 * kt + l32) * C::KROW + swz_pos(2 * s + h, l32, C::KROW, C::KCR) * 16);
+            sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[s], sacc[kt], 0, 0, 0);
+          }
+        }
+        // online softmax (lane: query qrow; keys 32kt + 8(v/4) + 4h + v%4 of the block)
+        const int kbase = cur_j * BK;
+        if (kbase + BK > N) {          // ragged last block: mask keys >= N
+          const int lim = N - kbase - 4 * h;
+#pragma unroll
+          for (int kt = 0; kt < C::NKT; ++kt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+              if (32 * kt + 8 * (v >> 2) + (v & 3) >= lim) sacc[kt][v] = -INFINITY;
+        }
+        float mloc = sacc[0][0];
 #pragma unroll
         for (int kt = 0; kt < C::NKT; ++kt)
 #pragma unroll
-          for (int v = 0; v < 16; ++v)
-            if (32 * kt + 8 * (v >> 2) + (v & 3) >= lim) sacc[kt][v] = -INFINITY;
-      }
-      float mloc = sacc[0][0];
-#pragma unroll
-      for (int kt = 0; kt < C::NKT; ++kt)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) mloc = fmaxf(mloc, sacc[kt][v]);
-      {
-        auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mloc), __float_as_uint(mloc), false, false);
-        mloc = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-      }
-      const float mb = mloc * sl2;
-      // rescale only when some row's maximum grew (wave-uniform branch); the largest
-      // weight of a row then stays exactly 1, so its bf16 copy carries no rounding error
-      if (__any(mb > m_run)) {
-        const float m_new = fmaxf(m_run, mb);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int m = 0; m < C::NM; ++m)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[m][i] *= alpha;
-      }
-      const float nm = -m_run;
-      float psum = 0.f;
-      bf16x8 pf[C::NKT][2];
-#pragma unroll
-      for (int kt = 0; kt < C::NKT; ++kt)
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) {
-          bf16x8 pv;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const float pe = __builtin_amdgcn_exp2f(fmaf(sacc[kt][8 * t2 + i], sl2, nm));
-            psum += pe;
-            pv[i] = (__bf16)pe;
-          }
-          pf[kt][t2] = pv;
+          for (int v = 0; v < 16; ++v) mloc = fmaxf(mloc, sacc[kt][v]);
+        {
+          auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mloc), __float_as_uint(mloc), false, false);
+          mloc = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
         }
-      l_run += psum;
-      // O^T += V^T P^T
+        const float mb = mloc * sl2;
+        // rescale only when some row's maximum grew (wave-uniform branch); the largest
+        // weight of a row then stays exactly 1, so its bf16 copy carries no rounding error
+        if (__any(mb > m_run)) {
+          const float m_new = fmaxf(m_run, mb);
+          const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+          m_run = m_new;
+          l_run *= alpha;
 #pragma unroll
-      for (int m = 0; m < C::NM; ++m)
+          for (int m = 0; m < C::NM; ++m)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) oacc[m][i] *= alpha;
+        }
+        const float nm = -m_run;
+        float psum = 0.f;
+        bf16x8 pf[C::NKT][2];
 #pragma unroll
         for (int kt = 0; kt < C::NKT; ++kt)
 #pragma unroll
           for (int t2 = 0; t2 < 2; ++t2) {
-            const bf16x8 va = *reinterpret_cast<const bf16x8 *>(
-                Vs + (32 * m + l32) * C::VROW + (((4 * kt + 2 * t2 + h) ^ vx) << 4));
-            oacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[kt][t2], oacc[m], 0, 0, 0);
+            bf16x8 pv;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              const float pe = __builtin_amdgcn_exp2f(fmaf(sacc[kt][8 * t2 + i], sl2, nm));
+              psum += pe;
+              pv[i] = (__bf16)pe;
+            }
+            pf[kt][t2] = pv;
           }
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();                 // Y: V tile free, K_{j+1} landed
-      if (jj + 1 < cnt) load_v(jn);
-      jb = jn;
+        l_run += psum;
+        // O^T += V^T P^T
+#pragma unroll
+        for (int m = 0; m < C::NM; ++m)
+#pragma unroll
+          for (int kt = 0; kt < C::NKT; ++kt)
+#pragma unroll
+            for (int t2 = 0; t2 < 2; ++t2) {
+              const bf16x8 va = *reinterpret_cast<const bf16x8 *>(
+                  vb + (32 * m + l32) * C::VROW + swz_pos(4 * kt + 2 * t2 + h, l32, C::VROW, C::VCR) * 16);
+              oacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[kt][t2], oacc[m], 0, 0, 0);
+            }
+      }
+      cur_j = nxt_j;
+      cur_m = nxt_m;
+      advance(nxt_j, nxt_m);
     }
+
     // finalise: l over both halves, O / l, store (lane: query qrow, dims 32m + 8a + 4h + b)
     {
       auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
       const float ltot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
       const float inv = 1.f / ltot;
-      if (qrow < N && out_f32) {
+      if (qlive && out_f32) {
         float *op = (float *)o + ((size_t)bh * N + qrow) * D + 4 * h;
 #pragma unroll
         for (int m = 0; m < C::NM; ++m)
@@ -424,7 +558,7 @@ __global__ __launch_bounds__(2 * BQ, 2) void k_attn_bf16(
           for (int a = 0; a < 4; ++a)
             *reinterpret_cast<f4 *>(op + 32 * m + 8 * a) =
                 f4{oacc[m][4 * a] * inv, oacc[m][4 * a + 1] * inv, oacc[m][4 * a + 2] * inv, oacc[m][4 * a + 3] * inv};
-      } else if (qrow < N) {
+      } else if (qlive) {
         uint16_t *op = (uint16_t *)o + ((size_t)bh * N + qrow) * D + 4 * h;
 #pragma unroll
         for (int m = 0; m < C::NM; ++m)
@@ -441,15 +575,16 @@ __global__ __launch_bounds__(2 * BQ, 2) void k_attn_bf16(
       trace[4 * (size_t)t + 0] = hw_id_word();
       trace[4 * (size_t)t + 1] = t_start;
       trace[4 * (size_t)t + 2] = t_end;
-      trace[4 * (size_t)t + 3] = (uint64_t)row;
+      trace[4 * (size_t)t + 3] = (uint64_t)u;
     }
   }
-  // The last workgroup to leave has seen every other workgroup's final ticket: reset the
-  // ticket and exit counters so the same plan can be run again.
+  // The last workgroup to leave has seen every other workgroup's final ticket: restore the
+  // ticket counters and the exit count so the same plan can be run again.
   if (tid == 0) {
     __threadfence();
     if (atomicAdd(&counter[1], 1) == (int)gridDim.x - 1) {
       atomicExch(&counter[0], 0);
+      for (int x = 0; x < 8; ++x) atomicExch(&counter[8 + x], counter[16 + x]);
       atomicExch(&counter[1], 0);
     }
   }
@@ -535,32 +670,33 @@ int launch_vt(const void *v, void *vt, int BH, int N, int D, int NKP, hipStream_
   return FVATTN_OK;
 }
 
-int launch_worklist(const int32_t *row_ptr, int rows, int nqb, int nkb, int sched, int32_t *wl, int32_t *counter,
-                    hipStream_t st) {
-  hipLaunchKernelGGL(k_worklist, dim3(1), dim3(1024), 0, st, row_ptr, rows, nqb, nkb, sched, wl, counter);
+int launch_worklist(const int32_t *row_ptr, int rows, int nqb, int nkb, int G, int sched, int32_t *wl,
+                    int32_t *counter, hipStream_t st) {
+  hipLaunchKernelGGL(k_worklist, dim3(1), dim3(1024), 0, st, row_ptr, rows, nqb, nkb, G, sched, wl, counter);
   FV_CHECK_LAUNCH();
   return FVATTN_OK;
 }
 
 template <int BQ, int BK, int D>
 static int launch_attn_bf16_t(const void *q, const void *k, const void *vt, void *o, int out_f32,
-                              const int32_t *row_ptr,
-                              const int32_t *col_idx, const int32_t *wl, int32_t *counter, int rows, int nqb,
-                              int N, int NKP, int grid, uint64_t *trace, hipStream_t st) {
-  using C = AttnCfg<BQ, BK, D>;
+                              const int32_t *row_ptr, const int32_t *col_idx, const int32_t *wl, int32_t *counter,
+                              int rows, int nqb, int N, int NKP, int grid, uint64_t *trace, hipStream_t st) {
   auto kern = k_attn_bf16<BQ, BK, D>;
+  constexpr int G = 128 / BQ;
+  const int ngroups = (nqb + G - 1) / G;
+  const int units = (rows / nqb) * ngroups;
   if (grid <= 0) {
     int dev = 0, cus = 0, occ = 0;
     if (hipGetDevice(&dev) != hipSuccess) return FVATTN_ERR_HIP;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return FVATTN_ERR_HIP;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, C::NT, 0) != hipSuccess) return FVATTN_ERR_HIP;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, 256, 0) != hipSuccess) return FVATTN_ERR_HIP;
     grid = cus * (occ > 0 ? occ : 1);
   }
-  if (grid > rows) grid = rows;
+  if (grid > units) grid = units;
   const float sl2 = (float)(1.4426950408889634 / sqrt((double)D));
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(C::NT), 0, st, (const uint16_t *)q, (const uint16_t *)k,
-                     (const uint16_t *)vt, o, out_f32, row_ptr, col_idx, wl, counter, rows, nqb, N, NKP, sl2,
-                     trace);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, st, (const uint16_t *)q, (const uint16_t *)k,
+                     (const uint16_t *)vt, o, out_f32, row_ptr, col_idx, wl, counter, units, ngroups, nqb, N, NKP,
+                     sl2, trace);
   FV_CHECK_LAUNCH();
   return FVATTN_OK;
 }
@@ -568,10 +704,10 @@ static int launch_attn_bf16_t(const void *q, const void *k, const void *vt, void
 int launch_attn_bf16(const void *q, const void *k, const void *vt, void *o, int out_f32, const int32_t *row_ptr,
                      const int32_t *col_idx, const int32_t *wl, int32_t *counter, int rows, int nqb, int N, int NKP,
                      int D, int BQ, int BK, int grid, uint64_t *trace, hipStream_t st) {
-#define FV_A(bq, bk, dd)                                                                                  \
-  if (BQ == bq && BK == bk && D == dd)                                                                    \
-    return launch_attn_bf16_t<bq, bk, dd>(q, k, vt, o, out_f32, row_ptr, col_idx, wl, counter, rows, nqb, N, NKP, grid, \
-                                          trace, st);
+#define FV_A(bq, bk, dd)                                                                                 \
+  if (BQ == bq && BK == bk && D == dd)                                                                   \
+    return launch_attn_bf16_t<bq, bk, dd>(q, k, vt, o, out_f32, row_ptr, col_idx, wl, counter, rows, nqb, N, \
+                                          NKP, grid, trace, st);
   FV_A(64, 64, 128) FV_A(128, 64, 128) FV_A(32, 64, 128) FV_A(64, 32, 128) FV_A(128, 32, 128) FV_A(32, 32, 128)
   FV_A(64, 64, 64) FV_A(128, 64, 64) FV_A(32, 64, 64) FV_A(64, 32, 64) FV_A(128, 32, 64) FV_A(32, 32, 64)
 #undef FV_A
