@@ -9,9 +9,9 @@ namespace fv {
 int launch_pool(const void *x, int BH, int N, int d, int dtype, int block, int layout, double *out,
                 int32_t *zero_me, int nzero, hipStream_t st);
 int launch_select(const double *qsw, const double *ksw, int BH, int d, int nqb, int nkb, double p,
-                  int32_t *counts, uint32_t *bitmask, int nkw, int32_t *head_load, hipStream_t st);
-int launch_csr(const int32_t *counts, const uint32_t *bitmask, int rows, int nkw, int32_t *row_ptr,
-               int32_t *col_idx, hipStream_t st);
+                  int32_t *counts, uint32_t *bitmask, int nkw, int32_t *head_load, int32_t *bsum, hipStream_t st);
+int launch_csr(const int32_t *counts, const uint32_t *bitmask, const int32_t *bsum, int rows, int nkw, int nkb,
+               int32_t *row_ptr, int32_t *col_idx, hipStream_t st);
 int launch_vt(const void *v, void *vt, int BH, int N, int D, int NKP, hipStream_t st);
 int launch_worklist(const int32_t *row_ptr, int rows, int nqb, int nkb, int G, int sched, int32_t *wl,
                     int32_t *counter, hipStream_t st);
@@ -58,6 +58,8 @@ struct RouteWs {
   double *qsw, *ksw;
   int32_t *counts;
   uint32_t *bitmask;
+  int32_t *bsum;   // per-64-row sums of counts
+  int nblk;
   size_t bytes;
 };
 
@@ -72,6 +74,9 @@ RouteWs route_ws_layout(const Shape &s, char *base) {
   off += align256((size_t)s.rows * sizeof(int32_t));
   w.bitmask = (uint32_t *)(base + off);
   off += align256((size_t)s.rows * s.nkw * sizeof(uint32_t));
+  w.nblk = (s.rows + 63) / 64;
+  w.bsum = (int32_t *)(base + off);
+  off += align256((size_t)w.nblk * sizeof(int32_t));
   w.bytes = off;
   return w;
 }
@@ -164,13 +169,13 @@ int fvattn_route(const void *q, const void *k, int B, int H, int N, int d, int d
   hipStream_t st = (hipStream_t)stream;
 
   csr->bh = s.BH; csr->n = N; csr->block_q = block_q; csr->block_k = block_k; csr->nqb = s.nqb; csr->nkb = s.nkb;
-  if ((rc = fv::launch_pool(q, s.BH, N, d, dtype, block_q, 1, w.qsw, nullptr, 0, st)) != FVATTN_OK) return rc;
+  if ((rc = fv::launch_pool(q, s.BH, N, d, dtype, block_q, 1, w.qsw, w.bsum, w.nblk, st)) != FVATTN_OK) return rc;
   if ((rc = fv::launch_pool(k, s.BH, N, d, dtype, block_k, 1, w.ksw, csr->head_load, s.BH, st)) != FVATTN_OK)
     return rc;
   if ((rc = fv::launch_select(w.qsw, w.ksw, s.BH, d, s.nqb, s.nkb, p, w.counts, w.bitmask, s.nkw, csr->head_load,
-                              st)) != FVATTN_OK)
+                              w.bsum, st)) != FVATTN_OK)
     return rc;
-  return fv::launch_csr(w.counts, w.bitmask, s.rows, s.nkw, csr->row_ptr, csr->col_idx, st);
+  return fv::launch_csr(w.counts, w.bitmask, w.bsum, s.rows, s.nkw, s.nkb, csr->row_ptr, csr->col_idx, st);
 }
 
 int fvattn_worklist(const fvattn_csr *csr, int schedule, int32_t *worklist, int32_t *counter, void *stream) {
