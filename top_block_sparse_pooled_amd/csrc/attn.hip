@@ -312,13 +312,16 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
   constexpr int G = 128 / BQ;     // query blocks per unit
   constexpr int WPQ = BQ / 32;    // waves per query block
   constexpr int NONE = 0x7fffffff;
+  constexpr int MAXW = 40;         // kept-block bitmap words (1280 key blocks)
   __shared__ __attribute__((aligned(1024))) uint8_t Ks[2 * C::KBYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t Vs[2 * C::VBYTES];
+  __shared__ uint32_t s_bm[G + 1][MAXW];   // kept key blocks of each query block; row G: union
   __shared__ int s_tile;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, kept in an SGPR
   const int wq = w / WPQ, wr = w % WPQ;                     // query block of the unit, 32-row slice
+  const int nkw = (N + BK * 32 - 1) / (BK * 32);             // bitmap words in use
   const int l32 = lane & 31, h = lane >> 5;
 
   // Tile loads: load i of wave w fills LDS bytes [(w*KI + i) KB, +1 KB) of a tile; lane L writes
@@ -404,27 +407,40 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
       }
     };
 
-    // merge of the unit's G ascending kept lists (identical in every thread)
-    int ptr[G], endp[G], hd[G];
+    // the unit's G kept lists as LDS bitmaps (one pass over col_idx per unit); the walk over
+    // their union is then a bit scan, and "does my query block keep it" a bit test
+    for (int i = tid; i < (G + 1) * MAXW; i += C::NT) (&s_bm[0][0])[i] = 0;
+    __syncthreads();
 #pragma unroll
     for (int gi = 0; gi < G; ++gi) {
-      ptr[gi] = gi < nrow ? row_ptr[r0 + gi] : 0;
-      endp[gi] = gi < nrow ? row_ptr[r0 + gi + 1] : 0;
-      hd[gi] = ptr[gi] < endp[gi] ? col_idx[ptr[gi]] : NONE;
-    }
-    auto advance = [&](int &jb, int &mask) {
-      jb = NONE;
-#pragma unroll
-      for (int gi = 0; gi < G; ++gi) jb = min(jb, hd[gi]);
-      mask = 0;
-      if (jb == NONE) return;
-#pragma unroll
-      for (int gi = 0; gi < G; ++gi)
-        if (hd[gi] == jb) {
-          mask |= 1 << gi;
-          ++ptr[gi];
-          hd[gi] = ptr[gi] < endp[gi] ? col_idx[ptr[gi]] : NONE;
+      if (gi < nrow) {
+        const int b0 = row_ptr[r0 + gi], b1 = row_ptr[r0 + gi + 1];
+        for (int e = b0 + tid; e < b1; e += C::NT) {
+          const int j = col_idx[e];
+          atomicOr(&s_bm[gi][j >> 5], 1u << (j & 31));
+          atomicOr(&s_bm[G][j >> 5], 1u << (j & 31));
         }
+      }
+    }
+    __syncthreads();
+    int uw = 0;                                   // union word index (uniform)
+    uint32_t ubits = (uint32_t)__builtin_amdgcn_readfirstlane(s_bm[G][0]);
+    auto advance = [&](int &jb, int &mask) {
+      while (ubits == 0u && uw + 1 < nkw) {
+        ++uw;
+        ubits = (uint32_t)__builtin_amdgcn_readfirstlane(s_bm[G][uw]);
+      }
+      if (ubits == 0u) {
+        jb = NONE;
+        mask = 0;
+        return;
+      }
+      jb = 32 * uw + (__ffs(ubits) - 1);
+      ubits &= ubits - 1u;
+      mask = 0;
+#pragma unroll
+      for (int gi = 0; gi < G; ++gi) mask |= (int)((s_bm[gi][uw] >> (jb & 31)) & 1u) << gi;
+      mask = __builtin_amdgcn_readfirstlane(mask);
     };
     int cur_j, cur_m, nxt_j, nxt_m;
     advance(cur_j, cur_m);
