@@ -6,8 +6,10 @@
 #include "common.h"
 
 namespace fv {
-int launch_pool(const void *x, int BH, int N, int d, int dtype, int block, int layout, double *out,
-                int32_t *zero_me, int nzero, hipStream_t st);
+int launch_pool(const void *x, int BH, int N, int d, int dtype, int block, double *out, hipStream_t st);
+int launch_pool_qk(const void *q, const void *k, int BH, int N, int d, int dtype, int block_q, int block_k,
+                   double *qsw, double *ksw, int32_t *zero0, int nzero0, int32_t *zero1, int nzero1,
+                   hipStream_t st);
 int launch_select(const double *qsw, const double *ksw, int BH, int d, int nqb, int nkb, double p,
                   int32_t *counts, uint32_t *bitmask, int nkw, int32_t *head_load, int32_t *bsum, hipStream_t st);
 int launch_csr(const int32_t *counts, const uint32_t *bitmask, const int32_t *bsum, int rows, int nkw, int nkb,
@@ -151,7 +153,7 @@ int fvattn_pool(const void *x, int BH, int N, int d, int dtype, int block, doubl
   if (BH > kMaxBH) return FVATTN_ERR_OVERFLOW;
   if ((long long)BH * N * d >= (1ll << 40)) return FVATTN_ERR_OVERFLOW;
   if (x == nullptr || out == nullptr) return FVATTN_ERR_INVALID;
-  return fv::launch_pool(x, BH, N, d, dtype, block, 0, out, nullptr, 0, (hipStream_t)stream);
+  return fv::launch_pool(x, BH, N, d, dtype, block, out, (hipStream_t)stream);
 }
 
 int fvattn_route(const void *q, const void *k, int B, int H, int N, int d, int dtype, int block_q, int block_k,
@@ -169,8 +171,8 @@ int fvattn_route(const void *q, const void *k, int B, int H, int N, int d, int d
   hipStream_t st = (hipStream_t)stream;
 
   csr->bh = s.BH; csr->n = N; csr->block_q = block_q; csr->block_k = block_k; csr->nqb = s.nqb; csr->nkb = s.nkb;
-  if ((rc = fv::launch_pool(q, s.BH, N, d, dtype, block_q, 1, w.qsw, w.bsum, w.nblk, st)) != FVATTN_OK) return rc;
-  if ((rc = fv::launch_pool(k, s.BH, N, d, dtype, block_k, 1, w.ksw, csr->head_load, s.BH, st)) != FVATTN_OK)
+  if ((rc = fv::launch_pool_qk(q, k, s.BH, N, d, dtype, block_q, block_k, w.qsw, w.ksw, w.bsum, w.nblk,
+                               csr->head_load, s.BH, st)) != FVATTN_OK)
     return rc;
   if ((rc = fv::launch_select(w.qsw, w.ksw, s.BH, d, s.nqb, s.nkb, p, w.counts, w.bitmask, s.nkw, csr->head_load,
                               w.bsum, st)) != FVATTN_OK)

@@ -48,6 +48,22 @@ __device__ __forceinline__ void unpack16(const u32x4 &c, float *out, float) {
 
 __host__ __device__ constexpr inline int cdiv(int a, int b) { return (a + b - 1) / b; }
 
+// Compute units of the current device (cached per device); 0 on success.
+inline int device_cus(int *cus) {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  if (dev >= 0 && dev < 64 && cache[dev] > 0) {
+    *cus = cache[dev];
+    return 0;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return -1;
+  if (dev >= 0 && dev < 64) cache[dev] = n;
+  *cus = n;
+  return 0;
+}
+
 }  // namespace fv
 
 // Returns FVATTN_ERR_HIP from the enclosing function if the last launch failed.

@@ -36,65 +36,102 @@ __device__ __forceinline__ size_t swz(int bh, int ngroups, int D, int j, int c) 
 }
 
 // ---------------------------------------------------------------------------------------
-// k_pool: x [BH][N][D] -> mean of every block of `block` tokens (real tokens only).
-// layout 0: plain [BH][nb][D]; layout 1: swizzled, nbp = nb rounded up to 16, padded
-// blocks written as zero.  grid = (cdiv(nbp, BPW), BH), 256 threads.
+// k_pool: x [BH][N][D] -> mean of every block of `block` tokens (real tokens only), for one
+// or two tensors (Q and K) in one launch.  Item = 16 consecutive blocks of one head of one
+// tensor; grid = (groups of tensor 0 + groups of tensor 1, BH), 256 threads.  Wave w pools
+// blocks w, w+4, w+8, w+12 of the group: lane l reads 16-byte chunk l % CPR of rows
+// l / CPR + RPL*i (16 loads in flight per lane), accumulates in float64 and the lanes of a
+// chunk are summed with cross-lane shuffles.  The 16 pooled rows are staged in LDS and
+// written as one contiguous run: layout 1 is the swizzled float64 MFMA operand order of
+// k_select (blocks past nb written as zero), layout 0 the plain [BH][nb][D] array.
 // ---------------------------------------------------------------------------------------
+struct PoolArgs {
+  const void *x[2];
+  double *out[2];
+  int block[2], nb[2], ngrp[2];   // ngrp = ceil(nb / 16); ngrp[1] = 0 for one tensor
+  int N, layout;
+  int32_t *zero[2];               // zeroed by workgroup (0, 0) (may be null)
+  int nzero[2];
+};
+
 template <typename T, int D>
-__global__ __launch_bounds__(256) void k_pool(const T *__restrict__ x, int N, int block, int nb,
-                                              int nbp, int layout, double *__restrict__ out,
-                                              int32_t *__restrict__ zero_me, int nzero) {
-  constexpr int EPC = DT<T>::per16;           // elements per 16-byte chunk
-  constexpr int CPR = D / EPC;                // chunks per row
-  constexpr int RPR = 256 / CPR;              // rows per load round
-  constexpr int MAXR = (128 + RPR - 1) / RPR; // rounds for the largest block (128)
-  __shared__ double red[RPR][D + 1];
+__global__ __launch_bounds__(256) void k_pool(PoolArgs a) {
+  constexpr int EPC = DT<T>::per16;   // elements per 16-byte chunk
+  constexpr int CPR = D / EPC;        // chunks per row
+  constexpr int RPL = 64 / CPR;       // rows covered by one wave-wide load
+  constexpr int NLD = 16;             // loads in flight per lane
+  constexpr int RPR = RPL * NLD;      // rows per round
+  __shared__ double stage[16][D + 1];
 
-  const int tid = threadIdx.x;
-  const int bh = blockIdx.y, j = blockIdx.x;  // one block per workgroup
-  const int ch = tid % CPR, r0 = tid / CPR;
-  if (zero_me != nullptr && j == 0 && bh == 0)
-    for (int i = tid; i < nzero; i += 256) zero_me[i] = 0;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int bh = blockIdx.y;
+  int gx = blockIdx.x;
+  const int t = gx < a.ngrp[0] ? 0 : 1;
+  if (t) gx -= a.ngrp[0];
+  if (blockIdx.x == 0 && bh == 0) {
+    for (int z = 0; z < 2; ++z)
+      if (a.zero[z] != nullptr)
+        for (int i = tid; i < a.nzero[z]; i += 256) a.zero[z][i] = 0;
+  }
+  const T *xh = reinterpret_cast<const T *>(a.x[t]) + (size_t)bh * a.N * D;
+  const int block = a.block[t], nb = a.nb[t], N = a.N;
+  const int c = lane % CPR, r = lane / CPR;
 
-  const T *xh = x + (size_t)bh * N * D;
-  const int s0 = j * block, e0 = min(s0 + block, N);
-  double acc[EPC];
+  for (int jj = w; jj < 16; jj += 4) {
+    const int j = gx * 16 + jj;
+    double acc[EPC];
 #pragma unroll
-  for (int t = 0; t < EPC; ++t) acc[t] = 0.0;
-  if (j < nb) {
-    u32x4 buf[MAXR];
+    for (int e = 0; e < EPC; ++e) acc[e] = 0.0;
+    int cnt = 1;
+    if (j < nb) {
+      const int s0 = j * block, e0 = min(s0 + block, N);
+      cnt = e0 - s0;
+      for (int base = s0; base < e0; base += RPR) {
+        u32x4 buf[NLD];
 #pragma unroll
-    for (int k = 0; k < MAXR; ++k) {
-      const int r = s0 + r0 + k * RPR;
-      buf[k] = u32x4{0u, 0u, 0u, 0u};
-      if (k * RPR < block && r < e0) buf[k] = *reinterpret_cast<const u32x4 *>(xh + (size_t)r * D + ch * EPC);
+        for (int i = 0; i < NLD; ++i) {
+          const int row = base + r + RPL * i;
+          buf[i] = u32x4{0u, 0u, 0u, 0u};
+          if (row < e0) buf[i] = *reinterpret_cast<const u32x4 *>(xh + (size_t)row * D + c * EPC);
+        }
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+          float f[EPC];
+          unpack16(buf[i], f, T());
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) acc[e] += (double)f[e];
+        }
+      }
     }
 #pragma unroll
-    for (int k = 0; k < MAXR; ++k) {
-      float f[EPC];
-      unpack16(buf[k], f, T());
+    for (int off = CPR; off < 64; off <<= 1)
 #pragma unroll
-      for (int t = 0; t < EPC; ++t) acc[t] += (double)f[t];
+      for (int e = 0; e < EPC; ++e) acc[e] += __shfl_xor(acc[e], off);
+    if (r == 0) {
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) stage[jj][c * EPC + e] = (j < nb) ? acc[e] / (double)cnt : 0.0;
     }
   }
-#pragma unroll
-  for (int t = 0; t < EPC; ++t) red[r0][ch * EPC + t] = acc[t];
   __syncthreads();
-  if (tid < D) {
-    double sum = 0.0;
-#pragma unroll 4
-    for (int r = 0; r < RPR; ++r) sum += red[r][tid];
-    const double mean = (j < nb) ? sum / (double)(e0 - s0) : 0.0;
-    if (layout)
-      out[swz(bh, nbp / 16, D, j, tid)] = mean;
-    else
-      out[((size_t)bh * nb + j) * D + tid] = mean;
+  double *out = a.out[t];
+  if (a.layout) {
+    // region of (bh, group): element (block jj, dim c) at (c/4)*64 + jj + 16*(c%4)
+    double *dst = out + ((size_t)bh * a.ngrp[t] + gx) * (D / 4) * 64;
+    for (int idx = tid; idx < 16 * D; idx += 256) {
+      const int jj = idx & 15, cc = ((idx >> 6) << 2) | ((idx >> 4) & 3);
+      dst[idx] = stage[jj][cc];
+    }
+  } else {
+    const int nrows = min(16, nb - gx * 16);
+    double *dst = out + ((size_t)bh * nb + gx * 16) * D;
+    for (int idx = tid; idx < nrows * D; idx += 256) dst[idx] = stage[idx / D][idx % D];
   }
 }
 
 // ---------------------------------------------------------------------------------------
-// k_select: scores, softmax, Top-p cut for 16 query blocks of one head.
-// grid = (nqbp/16, BH), 256 threads.  MAXT = key tiles (of 16) per wave.
+// k_select: scores, softmax, Top-p cut for 16 query blocks of one head per item.
+// Persistent: grid = min(resident workgroups, items), at least 8; 256 threads.
+// MAXT = key tiles (of 16) per wave.
 // Outputs counts[row] and the kept-bit mask bitmask[row][nkw]; adds loads to head_load.
 // ---------------------------------------------------------------------------------------
 constexpr int kMaxNkw = 40;  // 1280 key blocks
@@ -110,7 +147,8 @@ __global__ __launch_bounds__(256, MAXT <= 8 ? 2 : 1) void k_select(const double 
                                                 const double *__restrict__ ksw, int nqb, int nkb,
                                                 double scale, double p, int32_t *__restrict__ counts,
                                                 uint32_t *__restrict__ bitmask, int nkw,
-                                                int32_t *__restrict__ head_load, int32_t *__restrict__ bsum) {
+                                                int32_t *__restrict__ head_load, int32_t *__restrict__ bsum,
+                                                int BH) {
   constexpr int KS = D / 4;  // MFMA k-steps
   __shared__ uint32_t h_cnt[16][256];
   __shared__ unsigned long long h_mass[16][256];
@@ -125,9 +163,18 @@ __global__ __launch_bounds__(256, MAXT <= 8 ? 2 : 1) void k_select(const double 
   __shared__ int s_any;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int g = blockIdx.x, bh = blockIdx.y;
-  const int nqg = gridDim.x;
+  const int nqg = (nqb + 15) >> 4;
   const int nkt = (nkb + 15) >> 4;
+
+  // Persistent loop over items (head bh, group g of 16 query blocks).  Workgroup b runs on
+  // XCD b % 8 (round-robin dispatch); XCD x owns the x-th eighth of the items in head-major
+  // order, so its L2 holds the pooled keys of only a few heads.  gridDim.x >= 8.
+  const int items = BH * nqg;
+  const int xcd = blockIdx.x & 7;
+  const int nwx = ((int)gridDim.x - xcd + 7) >> 3;
+  const int it_end = (int)((long long)items * (xcd + 1) / 8);
+  for (int it = (int)((long long)items * xcd / 8) + (int)(blockIdx.x >> 3); it < it_end; it += nwx) {
+  const int bh = it / nqg, g = it - bh * nqg;
 
   // ---- scores: S[i][j] = sum_c qbar[i][c] * kbar[j][c], i = lane/16 + 4v, j = 16t + lane%16
   d4 acc[MAXT];
@@ -410,6 +457,8 @@ __global__ __launch_bounds__(256, MAXT <= 8 ? 2 : 1) void k_select(const double 
       atomicAdd(&bsum[row >> 6], c);   // per-64-row sums for the CSR scan
     }
   }
+  __syncthreads();   // LDS of this item fully consumed before the next item writes it
+  }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -468,50 +517,87 @@ __global__ __launch_bounds__(256) void k_csr(const int32_t *__restrict__ counts,
 // ---------------------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------------------
-template <typename T>
-static int launch_pool_t(const void *x, int BH, int N, int d, int block, int nb, int nbp, int layout,
-                         double *out, int32_t *zero_me, int nzero, hipStream_t st) {
-  const int nlim = layout ? nbp : nb;
-  dim3 grid(nlim, BH);
-  if (d == 128)
-    hipLaunchKernelGGL((k_pool<T, 128>), grid, dim3(256), 0, st, (const T *)x, N, block, nb, nbp, layout,
-                       out, zero_me, nzero);
-  else
-    hipLaunchKernelGGL((k_pool<T, 64>), grid, dim3(256), 0, st, (const T *)x, N, block, nb, nbp, layout,
-                       out, zero_me, nzero);
+static int launch_pool_args(const PoolArgs &pa, int BH, int d, int dtype, hipStream_t st) {
+  const dim3 grid(pa.ngrp[0] + pa.ngrp[1], BH);
+  if (dtype == FVATTN_BF16) {
+    if (d == 128) hipLaunchKernelGGL((k_pool<uint16_t, 128>), grid, dim3(256), 0, st, pa);
+    else hipLaunchKernelGGL((k_pool<uint16_t, 64>), grid, dim3(256), 0, st, pa);
+  } else {
+    if (d == 128) hipLaunchKernelGGL((k_pool<float, 128>), grid, dim3(256), 0, st, pa);
+    else hipLaunchKernelGGL((k_pool<float, 64>), grid, dim3(256), 0, st, pa);
+  }
   FV_CHECK_LAUNCH();
   return FVATTN_OK;
 }
 
-int launch_pool(const void *x, int BH, int N, int d, int dtype, int block, int layout, double *out,
-                int32_t *zero_me, int nzero, hipStream_t st) {
-  const int nb = cdiv(N, block);
-  const int nbp = cdiv(nb, 16) * 16;
-  if (dtype == FVATTN_BF16)
-    return launch_pool_t<uint16_t>(x, BH, N, d, block, nb, nbp, layout, out, zero_me, nzero, st);
-  return launch_pool_t<float>(x, BH, N, d, block, nb, nbp, layout, out, zero_me, nzero, st);
+int launch_pool(const void *x, int BH, int N, int d, int dtype, int block, double *out, hipStream_t st) {
+  PoolArgs pa = {};
+  pa.x[0] = x;
+  pa.out[0] = out;
+  pa.block[0] = block;
+  pa.nb[0] = cdiv(N, block);
+  pa.ngrp[0] = cdiv(pa.nb[0], 16);
+  pa.N = N;
+  pa.layout = 0;
+  return launch_pool_args(pa, BH, d, dtype, st);
+}
+
+int launch_pool_qk(const void *q, const void *k, int BH, int N, int d, int dtype, int block_q, int block_k,
+                   double *qsw, double *ksw, int32_t *zero0, int nzero0, int32_t *zero1, int nzero1,
+                   hipStream_t st) {
+  PoolArgs pa = {};
+  pa.x[0] = q;
+  pa.x[1] = k;
+  pa.out[0] = qsw;
+  pa.out[1] = ksw;
+  pa.block[0] = block_q;
+  pa.block[1] = block_k;
+  for (int t = 0; t < 2; ++t) {
+    pa.nb[t] = cdiv(N, pa.block[t]);
+    pa.ngrp[t] = cdiv(pa.nb[t], 16);
+  }
+  pa.N = N;
+  pa.layout = 1;
+  pa.zero[0] = zero0;
+  pa.nzero[0] = nzero0;
+  pa.zero[1] = zero1;
+  pa.nzero[1] = nzero1;
+  return launch_pool_args(pa, BH, d, dtype, st);
+}
+
+template <int D, int MT>
+static int launch_select_mt(const double *qsw, const double *ksw, int BH, int nqb, int nkb, double p,
+                            int32_t *counts, uint32_t *bitmask, int nkw, int32_t *head_load, int32_t *bsum,
+                            hipStream_t st) {
+  auto kern = k_select<D, MT>;
+  int cus = 0, occ = 0;
+  if (device_cus(&cus) != 0) return FVATTN_ERR_HIP;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, 256, 0) != hipSuccess) return FVATTN_ERR_HIP;
+  const int items = cdiv(nqb, 16) * BH;
+  int grid = cus * (occ > 0 ? occ : 1);
+  if (grid > items) grid = items;
+  if (grid < 8) grid = 8;   // every XCD range needs a worker
+  const double scale = 1.0 / sqrt((double)D);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, st, qsw, ksw, nqb, nkb, scale, p, counts, bitmask, nkw,
+                     head_load, bsum, BH);
+  FV_CHECK_LAUNCH();
+  return FVATTN_OK;
 }
 
 template <int D>
 static int launch_select_d(const double *qsw, const double *ksw, int BH, int nqb, int nkb, double p,
                            int32_t *counts, uint32_t *bitmask, int nkw, int32_t *head_load, int32_t *bsum,
                            hipStream_t st) {
-  const int nkt = cdiv(nkb, 16);
-  const int per_wave = cdiv(nkt, 4);
-  dim3 grid(cdiv(nqb, 16), BH);
-  const double scale = 1.0 / sqrt((double)D);
-#define FV_SEL(MT)                                                                             \
-  hipLaunchKernelGGL((k_select<D, MT>), grid, dim3(256), 0, st, qsw, ksw, nqb, nkb, scale, p, counts, \
-                     bitmask, nkw, head_load, bsum)
+  const int per_wave = cdiv(cdiv(nkb, 16), 4);
+#define FV_SEL(MT) \
+  return launch_select_mt<D, MT>(qsw, ksw, BH, nqb, nkb, p, counts, bitmask, nkw, head_load, bsum, st)
   if (per_wave <= 1) FV_SEL(1);
-  else if (per_wave <= 2) FV_SEL(2);
-  else if (per_wave <= 4) FV_SEL(4);
-  else if (per_wave <= 8) FV_SEL(8);
-  else if (per_wave <= 12) FV_SEL(12);
-  else FV_SEL(20);
+  if (per_wave <= 2) FV_SEL(2);
+  if (per_wave <= 4) FV_SEL(4);
+  if (per_wave <= 8) FV_SEL(8);
+  if (per_wave <= 12) FV_SEL(12);
+  FV_SEL(20);
 #undef FV_SEL
-  FV_CHECK_LAUNCH();
-  return FVATTN_OK;
 }
 
 int launch_select(const double *qsw, const double *ksw, int BH, int d, int nqb, int nkb, double p,
