@@ -313,8 +313,14 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
   constexpr int WPQ = BQ / 32;    // waves per query block
   constexpr int NONE = 0x7fffffff;
   constexpr int MAXW = 40;         // kept-block bitmap words (1280 key blocks)
-  __shared__ __attribute__((aligned(1024))) uint8_t Ks[2 * C::KBYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t Vs[2 * C::VBYTES];
+  // Two tile buffers per operand, as four separate LDS objects: the main loop is unrolled so
+  // that each half names its buffers statically, which lets the compiler see that the
+  // direct-to-LDS loads into one buffer never alias reads of the other (a single indexed
+  // array would make it wait for the prefetch before every read).
+  __shared__ __attribute__((aligned(1024))) uint8_t Ks0[C::KBYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t Ks1[C::KBYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t Vs0[C::VBYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t Vs1[C::VBYTES];
   __shared__ uint32_t s_bm[G + 1][MAXW];   // kept key blocks of each query block; row G: union
   __shared__ int s_tile;
 
@@ -376,9 +382,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
     const uint16_t *vth = vt + (size_t)bh * D * NKP;
     const __amdgpu_buffer_rsrc_t krs = buf_rsrc(kh, (uint32_t)N * D * 2);
     const __amdgpu_buffer_rsrc_t vrs = buf_rsrc(vth, (uint32_t)D * NKP * 2);
-    auto load_k = [&](int jb, int buf) {
+    auto load_k = [&](int jb, uint8_t *kbuf) {
       const uint32_t sbase = (uint32_t)jb * BK * D * 2 + (uint32_t)w * C::KI * C::KRPI * C::KROW;
-      uint8_t *dst = Ks + buf * C::KBYTES + w * C::KI * 1024;
+      uint8_t *dst = kbuf + w * C::KI * 1024;
 #pragma unroll
       for (int i = 0; i < C::KI; ++i) {
         uint32_t vo;
@@ -391,9 +397,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
         dma16(krs, vo, sbase + (uint32_t)i * C::KRPI * C::KROW, dst + i * 1024);
       }
     };
-    auto load_v = [&](int jb, int buf) {
+    auto load_v = [&](int jb, uint8_t *vbuf) {
       const uint32_t sbase = (uint32_t)jb * BK * 2 + (uint32_t)w * C::VI * C::VRPI * NKP * 2;
-      uint8_t *dst = Vs + buf * C::VBYTES + w * C::VI * 1024;
+      uint8_t *dst = vbuf + w * C::VI * 1024;
 #pragma unroll
       for (int i = 0; i < C::VI; ++i) {
         uint32_t vo;
@@ -446,8 +452,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
     advance(cur_j, cur_m);
     advance(nxt_j, nxt_m);
     if (cur_j != NONE) {
-      load_k(cur_j, 0);
-      load_v(cur_j, 0);
+      load_k(cur_j, Ks0);
+      load_v(cur_j, Vs0);
     }
 
     // this wave's query rows
@@ -471,17 +477,15 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
       for (int i = 0; i < 16; ++i) oacc[m][i] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;   // running row maximum (log2 units) and row sum
 
-    for (int st = 0; cur_j != NONE; ++st) {
-      const int b = st & 1;
+    // one key block: tiles of cur_j are in (kb, vb); the next block's are loaded into (kn, vn)
+    auto step = [&](const uint8_t *kb, const uint8_t *vb, uint8_t *kn, uint8_t *vn) {
       __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();                 // tiles of cur_j landed; buffer b^1 no longer read
+      __syncthreads();                 // tiles of cur_j landed; (kn, vn) no longer read
       if (nxt_j != NONE) {
-        load_k(nxt_j, b ^ 1);
-        load_v(nxt_j, b ^ 1);
+        load_k(nxt_j, kn);
+        load_v(nxt_j, vn);
       }
       if ((cur_m >> wq) & 1) {         // wave-uniform: this wave's query block kept cur_j
-        const uint8_t *kb = Ks + b * C::KBYTES;
-        const uint8_t *vb = Vs + b * C::VBYTES;
         // S^T tiles: 32 keys x 32 queries each
         f16v sacc[C::NKT];
 #pragma unroll
@@ -559,6 +563,11 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
       cur_j = nxt_j;
       cur_m = nxt_m;
       advance(nxt_j, nxt_m);
+    };
+    while (cur_j != NONE) {
+      step(Ks0, Vs0, Ks1, Vs1);
+      if (cur_j == NONE) break;
+      step(Ks1, Vs1, Ks0, Vs0);
     }
 
     // finalise: l over both halves, O / l, store (lane: query qrow, dims 32m + 8a + 4h + b)
