@@ -20,6 +20,8 @@
 //    V^T read cover the same keys;
 //  * persistent grid: workgroups pop tiles from a device work list through one atomic
 //    counter, so long rows start first and short rows fill the tail.
+#include <type_traits>
+
 #include "common.h"
 
 namespace fv {
@@ -394,7 +396,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
           const int gi = w * C::KI + i;
           vo = (uint32_t)(k_r0 * C::KROW + swz_pos(k_pos, gi * C::KRPI + k_r0, C::KROW, C::KCR) * 16);
         }
-        dma16(krs, vo, sbase + (uint32_t)i * C::KRPI * C::KROW, dst + i * 1024);
+        dma16(krs, vo + sbase + (uint32_t)i * C::KRPI * C::KROW, 0, dst + i * 1024);
       }
     };
     auto load_v = [&](int jb, uint8_t *vbuf) {
@@ -409,7 +411,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
           const int gi = w * C::VI + i;
           vo = (uint32_t)(v_r0 * NKP * 2 + swz_pos(v_pos, gi * C::VRPI + v_r0, C::VROW, C::VCR) * 16);
         }
-        dma16(vrs, vo, sbase + (uint32_t)i * C::VRPI * NKP * 2, dst + i * 1024);
+        dma16(vrs, vo + sbase + (uint32_t)i * C::VRPI * NKP * 2, 0, dst + i * 1024);
       }
     };
 
@@ -616,6 +618,423 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
 }
 
 // ---------------------------------------------------------------------------------------
+// bf16 MFMA attention for 64-key blocks, two wave groups per unit (k_attn_pp).
+//
+// A workgroup is 8 waves in two groups of 4.  Both groups cover the same 128 query rows (one
+// work unit, as in k_attn_bf16) and split the unit's ascending union of kept key blocks:
+// group g takes entries g, g+2, g+4, ... with its own online-softmax state, and the two
+// partial results (row maximum, row sum, O) are merged through LDS at the end of the unit.
+// Each group alternates two phases separated by workgroup barriers:
+//   M_i  S_i = K_i Q^T  and  O += V_{i-1} P_{i-1}            (MFMA)
+//   X_i  loads of K_{i+2} and V_{i+1};  P_i = softmax step of S_i   (VALU)
+// Group 1 starts one phase late, so on each SIMD one wave issues MFMAs while its partner
+// (the same SIMD slot of the other group) runs the exponentials.  K tiles are fetched two
+// steps ahead and V tiles one step ahead; buffers of each parity are separate LDS objects.
+// ---------------------------------------------------------------------------------------
+// Workgroup barrier for LDS hand-offs: the wave's own LDS operations complete, then s_barrier.
+// Deliberately no fence: a fence would also wait for the direct-to-LDS tile loads still in
+// flight, which the callers track themselves with wait_vmcnt.  The memory clobber keeps the
+// compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// s_waitcnt on the vector memory counter only (expcnt and lgkmcnt fields at their maxima).
+template <int NV>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(NV >= 0 && NV < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((NV & 15) | ((NV >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int BQ, int BK, int D>
+__global__ __launch_bounds__(512, 1) void k_attn_pp(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ vt,
+    void *__restrict__ o, int out_f32, const int32_t *__restrict__ row_ptr, const int32_t *__restrict__ col_idx,
+    const int32_t *__restrict__ worklist, int32_t *__restrict__ counter, int units, int ngroups, int nqb, int N,
+    int NKP, float sl2, uint64_t *__restrict__ trace) {
+  using C = AttnCfg<BK, D>;        // tile geometry; the 4 waves of a group load its tiles
+  static_assert(BK == 64, "64-key tiles (the merge reuses two K tiles as exchange area)");
+  constexpr int G = 128 / BQ;     // query blocks per unit
+  constexpr int WPQ = BQ / 32;    // waves per query block (within a group)
+  constexpr int MAXW = 40;        // kept-block bitmap words (1280 key blocks)
+  constexpr int NTH = 512;
+  constexpr int NH = C::NM / 2;   // 32-dim output tiles finalised by each group
+  __shared__ __attribute__((aligned(1024))) uint8_t K0[2][C::KBYTES];   // [group]; parity 0
+  __shared__ __attribute__((aligned(1024))) uint8_t K1[2][C::KBYTES];   // parity 1
+  __shared__ __attribute__((aligned(1024))) uint8_t V0[2][C::VBYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t V1[2][C::VBYTES];
+  __shared__ uint32_t s_bm[G + 1][MAXW];   // kept key blocks of each query block; row G: union
+  __shared__ int s_list[MAXW * 32];        // union, ascending: (key block << 4) | keeping query blocks
+  __shared__ float s_xm[2][4][64], s_xl[2][4][64];
+  __shared__ int s_n, s_tile;
+  static_assert(2 * C::KBYTES >= 4 * NH * 16 * 64 * 4, "exchange area");
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = w >> 2, wg = w & 3;                       // group, wave within the group
+  const int wq = wg / WPQ, wr = wg % WPQ;                   // query block of the unit, 32-row slice
+  const int nkw = (N + BK * 32 - 1) / (BK * 32);
+  const int l32 = lane & 31, h = lane >> 5;
+
+  const int k_r0 = lane / C::KCR, k_pos = lane % C::KCR;
+  const int v_r0 = lane / C::VCR, v_pos = lane % C::VCR;
+  uint32_t k_vo[C::KPER], v_vo[C::VPER];
+#pragma unroll
+  for (int j = 0; j < C::KPER; ++j) {
+    const int r = j * C::KRPI + k_r0;
+    k_vo[j] = (uint32_t)(k_r0 * C::KROW + swz_pos(k_pos, r, C::KROW, C::KCR) * 16);
+  }
+#pragma unroll
+  for (int j = 0; j < C::VPER; ++j) {
+    const int r = j * C::VRPI + v_r0;
+    v_vo[j] = (uint32_t)(v_r0 * NKP * 2 + swz_pos(v_pos, r, C::VROW, C::VCR) * 16);
+  }
+
+  const bool per_xcd = counter[2] != 0;
+  const int xcc = (int)(__builtin_amdgcn_s_getreg((31 << 11) | 20) & 7);   // XCC_ID
+  for (;;) {
+    if (tid == 0) {
+      int tk = units;
+      if (!per_xcd) {
+        tk = atomicAdd(&counter[0], 1);
+      } else {
+        for (int qq = 0; qq < 8; ++qq) {
+          const int x = (xcc + qq) & 7;
+          const int c = atomicAdd(&counter[8 + x], 1);
+          if (c < counter[17 + x]) {
+            tk = c;
+            break;
+          }
+        }
+      }
+      s_tile = tk;
+    }
+    __syncthreads();
+    const int t = s_tile;
+    __syncthreads();
+    if (t >= units) break;
+    uint64_t t_start = 0;
+    if (trace != nullptr) t_start = __builtin_amdgcn_s_memrealtime();
+
+    const int u = worklist[t];
+    const int bh = u / ngroups, g = u - bh * ngroups;
+    const int r0 = bh * nqb + g * G;
+    const int nrow = min(G, nqb - g * G);
+    const uint16_t *kh = k + (size_t)bh * N * D;
+    const uint16_t *vth = vt + (size_t)bh * D * NKP;
+    const __amdgpu_buffer_rsrc_t krs = buf_rsrc(kh, (uint32_t)N * D * 2);
+    const __amdgpu_buffer_rsrc_t vrs = buf_rsrc(vth, (uint32_t)D * NKP * 2);
+    // Tile loads of this group.  A negative block index loads from far outside the buffer:
+    // the range check returns zeros without touching memory, so every X phase issues the same
+    // number of loads and the vmcnt waits stay static.
+    constexpr uint32_t kFar = 0x7fff0000u;
+    auto load_k = [&](int jb, uint8_t *kbuf) {
+      const uint32_t sbase = jb < 0 ? kFar : (uint32_t)jb * BK * D * 2 + (uint32_t)wg * C::KI * C::KRPI * C::KROW;
+      uint8_t *dst = kbuf + wg * C::KI * 1024;
+#pragma unroll
+      for (int i = 0; i < C::KI; ++i) {
+        uint32_t vo;
+        if constexpr (C::KTAB) {
+          vo = k_vo[i % C::KPER];
+        } else {
+          const int gi = wg * C::KI + i;
+          vo = (uint32_t)(k_r0 * C::KROW + swz_pos(k_pos, gi * C::KRPI + k_r0, C::KROW, C::KCR) * 16);
+        }
+        dma16(krs, vo + sbase + (uint32_t)i * C::KRPI * C::KROW, 0, dst + i * 1024);
+      }
+    };
+    auto load_v = [&](int jb, uint8_t *vbuf) {
+      const uint32_t sbase = jb < 0 ? kFar : (uint32_t)jb * BK * 2 + (uint32_t)wg * C::VI * C::VRPI * NKP * 2;
+      uint8_t *dst = vbuf + wg * C::VI * 1024;
+#pragma unroll
+      for (int i = 0; i < C::VI; ++i) {
+        uint32_t vo;
+        if constexpr (C::VTAB) {
+          vo = v_vo[i % C::VPER];
+        } else {
+          const int gi = wg * C::VI + i;
+          vo = (uint32_t)(v_r0 * NKP * 2 + swz_pos(v_pos, gi * C::VRPI + v_r0, C::VROW, C::VCR) * 16);
+        }
+        dma16(vrs, vo + sbase + (uint32_t)i * C::VRPI * NKP * 2, 0, dst + i * 1024);
+      }
+    };
+
+    // this wave's query rows; loaded first, so the
+    // barriers of the list construction below retire them before the first tile load
+    const int qi = g * G + wq;
+    const int qrow = qi * BQ + 32 * wr + l32;
+    const bool qlive = qi < nqb && qrow < N;
+    bf16x8 qf[C::NS];
+    {
+      const uint16_t *qp = q + ((size_t)bh * N + (qlive ? qrow : 0)) * D + 8 * h;
+#pragma unroll
+      for (int s = 0; s < C::NS; ++s) {
+        u32x4 raw = {0u, 0u, 0u, 0u};
+        if (qlive) raw = *reinterpret_cast<const u32x4 *>(qp + 16 * s);
+        qf[s] = __builtin_bit_cast(bf16x8, raw);
+      }
+    }
+    // kept lists of the unit's query blocks as LDS bitmaps, then their union as a list
+    for (int i = tid; i < (G + 1) * MAXW; i += NTH) (&s_bm[0][0])[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) {
+      if (gi < nrow) {
+        const int b0 = row_ptr[r0 + gi], b1 = row_ptr[r0 + gi + 1];
+        for (int e = b0 + tid; e < b1; e += NTH) {
+          const int j = col_idx[e];
+          atomicOr(&s_bm[gi][j >> 5], 1u << (j & 31));
+          atomicOr(&s_bm[G][j >> 5], 1u << (j & 31));
+        }
+      }
+    }
+    __syncthreads();
+    if (w == 0) {
+      const uint32_t word = lane < nkw ? s_bm[G][lane] : 0u;
+      const int pc = __popc(word);
+      int incl = pc;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int ov = __shfl_up(incl, off);
+        if (lane >= off) incl += ov;
+      }
+      int pos = incl - pc;
+      uint32_t wd = word;
+      while (wd != 0u) {
+        const int bit = __ffs(wd) - 1;
+        wd &= wd - 1u;
+        int msk = 0;
+#pragma unroll
+        for (int gi = 0; gi < G; ++gi) msk |= (int)((s_bm[gi][lane] >> bit) & 1u) << gi;
+        s_list[pos++] = ((32 * lane + bit) << 4) | msk;
+      }
+      if (lane == 63) s_n = incl;
+    }
+    __syncthreads();
+    const int n = s_n;
+    const int S = (n + 1) >> 1;                   // steps of either group
+    auto entry = [&](int i) -> int {              // list entry of this group's step i, or -1
+      const int e = 2 * i + grp;
+      return e < n ? __builtin_amdgcn_readfirstlane(s_list[e]) : -1;
+    };
+
+    int ep = -1, ec = entry(0), e1 = entry(1);   // entries of steps i-1, i, i+1
+    // prologue in the order a previous X phase would use: K_0, then K_1 and V_0
+    load_k(ec >> 4, K0[grp]);      // (entry -1 >> 4 = -1: an empty load)
+    load_k(e1 >> 4, K1[grp]);
+    load_v(ec >> 4, V0[grp]);
+
+    f16v oacc[C::NM];
+#pragma unroll
+    for (int m = 0; m < C::NM; ++m)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[m][i] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;
+    bf16x8 pf[C::NKT][2];
+#pragma unroll
+    for (int kt = 0; kt < C::NKT; ++kt) pf[kt][0] = pf[kt][1] = bf16x8{};
+
+    if (grp == 1) lds_barrier();   // group 1 runs one phase behind group 0
+
+    // M_i: kb holds K_i, vbp holds V_{i-1}.  X_i loads K_{i+2} into kdst (the buffer of K_i)
+    // and V_{i+1} into vdst (the buffer of V_{i-1}).  The loop is rotated so that its header
+    // sits before an X phase (no tile reads there).
+    f16v sacc[C::NKT];
+    bool dos = false;
+    auto phaseM = [&](const uint8_t *kb, const uint8_t *vbp) {
+      // K_i and V_{i-1} landed: only the previous X phase's loads (K_{i+1}, then V_i) may
+      // still be in flight
+      wait_vmcnt<C::KI + C::VI>();
+      lds_barrier();
+      dos = ec >= 0 && ((ec >> wq) & 1);
+      const bool dop = ep >= 0 && ((ep >> wq) & 1);
+      // Consecutive MFMAs go to independent accumulators (the NKT chains of S, the NM chains
+      // of O).  Operands come from a ring of RING fragments read from LDS RING MFMAs ahead;
+      // sched_barrier keeps the compiler from sinking the reads back to their uses.
+      constexpr int RING = 4;
+      if (dos) {
+        constexpr int NT_S = C::NS * C::NKT;   // MFMA t: k-step t / NKT, key tile t % NKT
+        auto kaddr = [&](int t) {
+          const int s = t / C::NKT, kt = t % C::NKT;
+          return reinterpret_cast<const bf16x8 *>(kb + (32 * kt + l32) * C::KROW +
+                                                  swz_pos(2 * s + h, l32, C::KROW, C::KCR) * 16);
+        };
+        bf16x8 fr[RING];
+#pragma unroll
+        for (int t = 0; t < RING; ++t) fr[t] = *kaddr(t);
+#pragma unroll
+        for (int kt = 0; kt < C::NKT; ++kt)
+#pragma unroll
+          for (int i2 = 0; i2 < 16; ++i2) sacc[kt][i2] = 0.f;
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < NT_S; ++t) {
+          sacc[t % C::NKT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[t % RING], qf[t / C::NKT], sacc[t % C::NKT], 0, 0, 0);
+          if (t + RING < NT_S) fr[t % RING] = *kaddr(t + RING);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      if (dop) {
+        constexpr int NT_P = C::NKT * 2 * C::NM;   // MFMA t: (kt, t2) = t / NM, output tile t % NM
+        auto vaddr = [&](int t) {
+          const int kk = t / C::NM, m = t % C::NM;
+          return reinterpret_cast<const bf16x8 *>(vbp + (32 * m + l32) * C::VROW +
+                                                  swz_pos(2 * kk + h, l32, C::VROW, C::VCR) * 16);
+        };
+        bf16x8 fr[RING];
+#pragma unroll
+        for (int t = 0; t < RING; ++t) fr[t] = *vaddr(t);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < NT_P; ++t) {
+          const int kk = t / C::NM;
+          oacc[t % C::NM] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[t % RING], pf[kk >> 1][kk & 1], oacc[t % C::NM], 0, 0, 0);
+          if (t + RING < NT_P) fr[t % RING] = *vaddr(t + RING);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    };
+    auto phaseX = [&](int i, uint8_t *kdst, uint8_t *vdst) {
+      lds_barrier();
+      // ---- X_i
+      const int e2 = entry(i + 2);
+      load_k(e2 >> 4, kdst);
+      load_v(e1 >> 4, vdst);
+      if (dos) {
+        // online softmax (lane: query qrow; keys 32kt + 8(v/4) + 4h + v%4 of the block)
+        const int kbase = (ec >> 4) * BK;
+        if (kbase + BK > N) {
+          const int lim = N - kbase - 4 * h;
+#pragma unroll
+          for (int kt = 0; kt < C::NKT; ++kt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+              if (32 * kt + 8 * (v >> 2) + (v & 3) >= lim) sacc[kt][v] = -INFINITY;
+        }
+        float mloc = sacc[0][0];
+#pragma unroll
+        for (int kt = 0; kt < C::NKT; ++kt)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) mloc = fmaxf(mloc, sacc[kt][v]);
+        {
+          auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mloc), __float_as_uint(mloc), false, false);
+          mloc = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        }
+        const float mb = mloc * sl2;
+        // rescale only when some row's maximum grew (wave-uniform branch); the largest
+        // weight of a row then stays exactly 1, so its bf16 copy carries no rounding error
+        if (__any(mb > m_run)) {
+          const float m_new = fmaxf(m_run, mb);
+          const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+          m_run = m_new;
+          l_run *= alpha;
+#pragma unroll
+          for (int m = 0; m < C::NM; ++m)
+#pragma unroll
+            for (int i2 = 0; i2 < 16; ++i2) oacc[m][i2] *= alpha;
+        }
+        const float nm = -m_run;
+        float psum = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < C::NKT; ++kt)
+#pragma unroll
+          for (int t2 = 0; t2 < 2; ++t2) {
+            bf16x8 pv;
+#pragma unroll
+            for (int i2 = 0; i2 < 8; ++i2) {
+              const float pe = __builtin_amdgcn_exp2f(fmaf(sacc[kt][8 * t2 + i2], sl2, nm));
+              psum += pe;
+              pv[i2] = (__bf16)pe;
+            }
+            pf[kt][t2] = pv;
+          }
+        l_run += psum;
+      }
+      ep = ec;
+      ec = e1;
+      e1 = e2;
+    };
+    phaseM(K0[grp], V1[grp]);                      // M_0
+    for (int i = 0; i < S; i += 2) {
+      phaseX(i, K0[grp], V1[grp]);
+      phaseM(K1[grp], V0[grp]);                    // M_{i+1}
+      if (i + 1 == S) break;
+      phaseX(i + 1, K1[grp], V0[grp]);
+      phaseM(K0[grp], V1[grp]);                    // M_{i+2}
+    }
+    if (grp == 0) lds_barrier();   // equal barrier counts for both groups
+    lds_barrier();                 // both groups are past their last phase: tile buffers free
+
+    // ---- merge: group g finalises output tiles [g*NH, g*NH + NH) and hands the partner
+    // (same rows, other group) the other tiles through LDS.  The group number is made a
+    // compile-time constant so that the accumulators are indexed statically.
+    auto merge = [&](auto gc) {
+      constexpr int GG = decltype(gc)::value;
+      {
+        float *xo = reinterpret_cast<float *>(GG == 0 ? &K0[0][0] : &K1[0][0]);
+#pragma unroll
+        for (int mm = 0; mm < NH; ++mm)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) xo[((wg * NH + mm) * 16 + i) * 64 + lane] = oacc[(GG ^ 1) * NH + mm][i];
+        s_xm[GG][wg][lane] = m_run;
+        s_xl[GG][wg][lane] = l_run;
+      }
+      lds_barrier();
+      const float *xi = reinterpret_cast<const float *>(GG == 0 ? &K1[0][0] : &K0[0][0]);
+      const float m2 = s_xm[GG ^ 1][wg][lane], l2 = s_xl[GG ^ 1][wg][lane];
+      const float mx = fmaxf(m_run, m2);
+      const float a1 = mx == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mx);
+      const float a2 = mx == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m2 - mx);
+      const float lp = a1 * l_run + a2 * l2;
+      auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lp), __float_as_uint(lp), false, false);
+      const float inv = 1.f / (__uint_as_float(sw[0]) + __uint_as_float(sw[1]));
+      f16v res[NH];
+#pragma unroll
+      for (int mm = 0; mm < NH; ++mm)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          res[mm][i] = (a1 * oacc[GG * NH + mm][i] + a2 * xi[((wg * NH + mm) * 16 + i) * 64 + lane]) * inv;
+      // store (lane: query qrow, dims 32m + 8a + 4h + b)
+      if (qlive && out_f32) {
+        float *op = (float *)o + ((size_t)bh * N + qrow) * D + 4 * h;
+#pragma unroll
+        for (int mm = 0; mm < NH; ++mm)
+#pragma unroll
+          for (int a = 0; a < 4; ++a)
+            *reinterpret_cast<f4 *>(op + 32 * (GG * NH + mm) + 8 * a) =
+                f4{res[mm][4 * a], res[mm][4 * a + 1], res[mm][4 * a + 2], res[mm][4 * a + 3]};
+      } else if (qlive) {
+        uint16_t *op = (uint16_t *)o + ((size_t)bh * N + qrow) * D + 4 * h;
+#pragma unroll
+        for (int mm = 0; mm < NH; ++mm)
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            const uint32_t w0 = pack_bf16(res[mm][4 * a], res[mm][4 * a + 1]);
+            const uint32_t w1 = pack_bf16(res[mm][4 * a + 2], res[mm][4 * a + 3]);
+            *reinterpret_cast<u32x2 *>(op + 32 * (GG * NH + mm) + 8 * a) = u32x2{w0, w1};
+          }
+      }
+    };
+    if (grp == 0) merge(std::integral_constant<int, 0>{});
+    else merge(std::integral_constant<int, 1>{});
+    if (trace != nullptr && tid == 0) {
+      const uint64_t t_end = __builtin_amdgcn_s_memrealtime();
+      trace[4 * (size_t)t + 0] = hw_id_word();
+      trace[4 * (size_t)t + 1] = t_start;
+      trace[4 * (size_t)t + 2] = t_end;
+      trace[4 * (size_t)t + 3] = (uint64_t)u;
+    }
+  }
+  // The last workgroup to leave restores the ticket counters and the exit count.
+  if (tid == 0) {
+    __threadfence();
+    if (atomicAdd(&counter[1], 1) == (int)gridDim.x - 1) {
+      atomicExch(&counter[0], 0);
+      for (int x = 0; x < 8; ++x) atomicExch(&counter[8 + x], counter[16 + x]);
+      atomicExch(&counter[1], 0);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
 // float32 attention: one thread per query row, K/V tiles through LDS, online softmax in
 // float32.  grid = rows (tile t processes worklist[t]).
 // ---------------------------------------------------------------------------------------
@@ -706,20 +1125,21 @@ template <int BQ, int BK, int D>
 static int launch_attn_bf16_t(const void *q, const void *k, const void *vt, void *o, int out_f32,
                               const int32_t *row_ptr, const int32_t *col_idx, const int32_t *wl, int32_t *counter,
                               int rows, int nqb, int N, int NKP, int grid, uint64_t *trace, hipStream_t st) {
-  auto kern = k_attn_bf16<BQ, BK, D>;
+  // 64-key blocks: two wave groups per unit (k_attn_pp); 32-key blocks: k_attn_bf16
+  auto kern = BK == 64 ? k_attn_pp<BQ, 64, D> : k_attn_bf16<BQ, BK, D>;
+  const int nthreads = BK == 64 ? 512 : 256;
   constexpr int G = 128 / BQ;
   const int ngroups = (nqb + G - 1) / G;
   const int units = (rows / nqb) * ngroups;
   if (grid <= 0) {
-    int dev = 0, cus = 0, occ = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return FVATTN_ERR_HIP;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return FVATTN_ERR_HIP;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, 256, 0) != hipSuccess) return FVATTN_ERR_HIP;
+    int cus = 0, occ = 0;
+    if (device_cus(&cus) != 0) return FVATTN_ERR_HIP;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, nthreads, 0) != hipSuccess) return FVATTN_ERR_HIP;
     grid = cus * (occ > 0 ? occ : 1);
   }
   if (grid > units) grid = units;
   const float sl2 = (float)(1.4426950408889634 / sqrt((double)D));
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, st, (const uint16_t *)q, (const uint16_t *)k,
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(nthreads), 0, st, (const uint16_t *)q, (const uint16_t *)k,
                      (const uint16_t *)vt, o, out_f32, row_ptr, col_idx, wl, counter, units, ngroups, nqb, N, NKP,
                      sl2, trace);
   FV_CHECK_LAUNCH();
