@@ -112,7 +112,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="wan14b_n32760")
     ap.add_argument("--p", type=float, default=None)
-    ap.add_argument("--schedule", default="xcd", choices=["lpt", "identity", "head_lpt", "xcd"])
+    ap.add_argument("--schedule", default="identity", choices=["lpt", "identity", "head_lpt", "xcd"])
     ap.add_argument("--out", default="f32", choices=["f32", "bf16"],
                     help="output dtype of the attention (f32 = accumulator precision)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)

@@ -846,6 +846,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_pp(
       lds_barrier();
       dos = ec >= 0 && ((ec >> wq) & 1);
       const bool dop = ep >= 0 && ((ep >> wq) & 1);
+      __builtin_amdgcn_s_setprio(2);   // MFMA issue ahead of the partner wave's VALU work
       // Consecutive MFMAs go to independent accumulators (the NKT chains of S, the NM chains
       // of O).  Operands come from a ring of RING fragments read from LDS RING MFMAs ahead;
       // sched_barrier keeps the compiler from sinking the reads back to their uses.
@@ -891,6 +892,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_pp(
           __builtin_amdgcn_sched_barrier(0);
         }
       }
+      __builtin_amdgcn_s_setprio(0);
     };
     auto phaseX = [&](int i, uint8_t *kdst, uint8_t *vdst) {
       lds_barrier();
@@ -919,34 +921,43 @@ __global__ __launch_bounds__(512, 1) void k_attn_pp(
           mloc = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
         }
         const float mb = mloc * sl2;
-        // rescale only when some row's maximum grew (wave-uniform branch); the largest
-        // weight of a row then stays exactly 1, so its bf16 copy carries no rounding error
-        if (__any(mb > m_run)) {
+        // Lazy rescale (wave-uniform branch): the reference maximum m_run is raised only when
+        // some row's maximum exceeds it by more than kLazy (log2 units), so weights stay
+        // below 2^kLazy and O is rescaled a few times per unit instead of at most steps.  The
+        // row sum adds the bf16 weights that P.V uses, so O / l is an exact weighted mean of
+        // those weights and their rounding cancels in the largest ones.
+        constexpr float kLazy = 8.f;
+        if (__any(mb > m_run + kLazy)) {
           const float m_new = fmaxf(m_run, mb);
-          const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+          if (m_run != -INFINITY) {
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            l_run *= alpha;
+#pragma unroll
+            for (int m = 0; m < C::NM; ++m)
+#pragma unroll
+              for (int i2 = 0; i2 < 16; ++i2) oacc[m][i2] *= alpha;
+          }
           m_run = m_new;
-          l_run *= alpha;
-#pragma unroll
-          for (int m = 0; m < C::NM; ++m)
-#pragma unroll
-            for (int i2 = 0; i2 < 16; ++i2) oacc[m][i2] *= alpha;
         }
         const float nm = -m_run;
-        float psum = 0.f;
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+        float ps[2] = {0.f, 0.f};
 #pragma unroll
         for (int kt = 0; kt < C::NKT; ++kt)
 #pragma unroll
           for (int t2 = 0; t2 < 2; ++t2) {
             bf16x8 pv;
 #pragma unroll
-            for (int i2 = 0; i2 < 8; ++i2) {
-              const float pe = __builtin_amdgcn_exp2f(fmaf(sacc[kt][8 * t2 + i2], sl2, nm));
-              psum += pe;
-              pv[i2] = (__bf16)pe;
-            }
+            for (int i2 = 0; i2 < 8; ++i2) pv[i2] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[kt][8 * t2 + i2], sl2, nm));
             pf[kt][t2] = pv;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const bf16x2 pr = {pv[2 * j], pv[2 * j + 1]};
+              ps[t2] = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, ps[t2], false);
+            }
           }
-        l_run += psum;
+        l_run += ps[0] + ps[1];
       }
       ep = ec;
       ec = e1;
