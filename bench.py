@@ -250,7 +250,7 @@ def main():
                     schedule=args.schedule, out=args.out, nnz=nnz, kept_frac=nnz / (w.rows * w.nkb),
                     executed_tflop=flops / 1e12, nominal_tflop=flops_nominal / 1e12),
         stages_ms=dict(route=route_ms, plan=plan_ms, attn=attn_ms),
-        roofline=dict(bound="mfma", kernel="k_attn_bf16", achieved=attn_tflops, peak=PEAK_BF16_TFLOPS,
+        roofline=dict(bound="mfma", kernel=attn_kernel_name(w), achieved=attn_tflops, peak=PEAK_BF16_TFLOPS,
                       unit="TFLOP/s", frac=attn_tflops / PEAK_BF16_TFLOPS, traffic=traffic),
         routing=dict(bound="hbm", achieved=route_gbps, peak=PEAK_HBM_GBPS, unit="GB/s",
                      frac=route_gbps / PEAK_HBM_GBPS, algorithmic_bytes=route_bytes, us=1e3 * route_ms),
@@ -258,6 +258,14 @@ def main():
         **extras,
     )
     print(json.dumps(rec), flush=True)
+
+
+def attn_kernel_name(w):
+    """The bf16 attention kernel the library runs for this workload (64-key blocks: two
+    wave groups per unit; 32-key blocks: one group)."""
+    if w.dtype != "bf16":
+        return "k_attn_f32"
+    return "k_attn_pp" if w.block_k == 64 else "k_attn_bf16"
 
 
 def _attn_source_sha():
