@@ -99,20 +99,61 @@ def topp_count(P_sorted_row: np.ndarray, p: float) -> int:
     return int(hit[0]) + 1 if hit.size else n
 
 
+# --------------------------------------------------------------------------
+# Routing variants (the hot path's next rows).  [FVAttn] contrasts Top-p with a
+# fixed Top-k; [TUTOR] 5.2 keeps the top-k key blocks by pooled score and adds
+# a local window of neighbouring blocks as a floor.  Readings:
+#   * mode "topk": the first min(k, nkb) blocks of the descending order (the
+#     same order and tie rule as Top-p; softmax is monotone, so this is the
+#     top-k by pooled score);
+#   * a clamp k_min <= k* <= k_max on the Top-p count (k_max = 0: none), taken
+#     as the first k* blocks of the order;
+#   * window w > 0: key blocks within w blocks of those that overlap the query
+#     block's token span are always kept (union with the selection); w = 0 adds
+#     nothing.  With equal block sizes this is [TUTOR]'s i-w .. i+w.
+# --------------------------------------------------------------------------
+def selection_count(P_sorted_row: np.ndarray, mode: str = "topp", p: float = 0.9,
+                    topk: int = 0, k_min: int = 1, k_max: int = 0) -> int:
+    """Number of leading blocks of the descending order the selection keeps."""
+    n = P_sorted_row.shape[0]
+    if mode == "topk":
+        return min(int(topk), n)
+    c = topp_count(P_sorted_row, p)
+    c = max(c, int(k_min))
+    if k_max > 0:
+        c = min(c, int(k_max))
+    return min(c, n)
+
+
+def window_blocks(i: int, n_tokens: int, block_q: int, block_k: int, window: int) -> np.ndarray:
+    """Key blocks forced by a local window of `window` blocks around query block i."""
+    if window <= 0:
+        return np.zeros(0, dtype=np.int64)
+    nkb = -(-n_tokens // block_k)
+    s0, e0 = i * block_q, min((i + 1) * block_q, n_tokens)
+    jlo, jhi = s0 // block_k, (e0 - 1) // block_k      # key blocks overlapping the span
+    return np.arange(max(0, jlo - window), min(nkb - 1, jhi + window) + 1, dtype=np.int64)
+
+
 def route_head(q_h: np.ndarray, k_h: np.ndarray, block_q: int, block_k: int, p: float,
-               diagnostics: bool = False):
+               diagnostics: bool = False, mode: str = "topp", topk: int = 0, k_min: int = 1,
+               k_max: int = 0, window: int = 0):
     """Routing of one head: q_h, k_h [N, d].  Returns (kept, extra) where kept is a
     list over query blocks of ascending int arrays of kept key-block indices.
-    With diagnostics, extra = dict(order, cum, counts, P)."""
+    With diagnostics, extra = dict(order, cum, counts, P).  mode / topk / k_min /
+    k_max / window select a routing variant (defaults: plain Top-p)."""
     qbar = pool_blocks(q_h, block_q)
     kbar = pool_blocks(k_h, block_k)
     P = block_importance(block_scores(qbar, kbar))
     order = routing_order(P)
+    N = q_h.shape[0]
     kept, counts, cums = [], [], []
     for i in range(P.shape[0]):
         Ps = P[i, order[i]]
-        c = topp_count(Ps, p)
-        kept.append(np.sort(order[i, :c]).astype(np.int64))
+        c = selection_count(Ps, mode, p, topk, k_min, k_max)
+        sel = order[i, :c]
+        win = window_blocks(i, N, block_q, block_k, window)
+        kept.append(np.union1d(sel, win).astype(np.int64))
         counts.append(c)
         if diagnostics:
             cums.append(np.cumsum(Ps))
@@ -137,13 +178,14 @@ def csr_rows(kept_per_head: Sequence[Sequence[np.ndarray]]):
 
 
 def route(q: np.ndarray, k: np.ndarray, block_q: int, block_k: int, p: float,
-          diagnostics: bool = False):
-    """q, k [B, H, N, d] -> dict(row_ptr, col_idx, head_load, nnz[, per-head diagnostics])."""
+          diagnostics: bool = False, **variant):
+    """q, k [B, H, N, d] -> dict(row_ptr, col_idx, head_load, nnz[, per-head diagnostics]).
+    `variant` (mode, topk, k_min, k_max, window) selects a routing variant."""
     B, H, N, d = q.shape
     kept_all, diags = [], []
     for b in range(B):
         for h in range(H):
-            kept, extra = route_head(q[b, h], k[b, h], block_q, block_k, p, diagnostics)
+            kept, extra = route_head(q[b, h], k[b, h], block_q, block_k, p, diagnostics, **variant)
             kept_all.append(kept)
             diags.append(extra)
     row_ptr, col_idx, head_load = csr_rows(kept_all)
