@@ -107,6 +107,37 @@ typedef struct fvattn_attn_opts {
   int32_t reserved;
 } fvattn_attn_opts;
 
+/* Routing variants of fvattn_route_ex. */
+enum {
+  FVATTN_ROUTE_TOPP = 0, /* Top-p: shortest prefix of the descending order with mass >= p  */
+  FVATTN_ROUTE_TOPK = 1  /* fixed top-k: the first min(topk, nkb) blocks of that order      */
+};
+
+/*
+ * Options of fvattn_route_ex.  The FVAttn summary contrasts Top-p routing with a fixed
+ * Top-k; the tutorial's block-sparse section (5.2) keeps the top-k key blocks by pooled score
+ * and adds a local window of neighbouring blocks.  Both use the same importance and the same
+ * descending order (ties to the lower block index) as Top-p.
+ *   mode    FVATTN_ROUTE_TOPP or FVATTN_ROUTE_TOPK
+ *   p       Top-p threshold in (0, 1] (mode TOPP)
+ *   topk    blocks per row, >= 1 (mode TOPK; more than nkb keeps every block)
+ *   k_min   mode TOPP: the Top-p count is raised to at least k_min (>= 1) ...
+ *   k_max   ... and lowered to at most k_max (0 = no upper bound; else >= k_min); the kept
+ *           blocks are then the first clamp(count) blocks of the order
+ *   window  >= 0: key blocks within `window` blocks of those that overlap the query block's
+ *           tokens are always kept, in addition to the selection (0 = none).  With equal
+ *           block sizes this is query block i's neighbours i-window .. i+window.
+ */
+typedef struct fvattn_route_opts {
+  int32_t mode;
+  int32_t topk;
+  double p;
+  int32_t k_min;
+  int32_t k_max;
+  int32_t window;
+  int32_t reserved;
+} fvattn_route_opts;
+
 /* Library version (FVATTN_VERSION of the build). */
 int fvattn_version(void);
 
@@ -145,6 +176,16 @@ int fvattn_pool(const void *x, int BH, int N, int d, int dtype, int block, doubl
 int fvattn_route(const void *q, const void *k, int B, int H, int N, int d, int dtype,
                  int block_q, int block_k, double p, fvattn_csr *csr, void *ws,
                  size_t ws_bytes, void *stream);
+
+/*
+ * fvattn_route with a routing variant (opts, not NULL; see fvattn_route_opts).  Same
+ * arguments, outputs, workspace and errors as fvattn_route; invalid options return
+ * FVATTN_ERR_INVALID.  fvattn_route(..., p, ...) equals fvattn_route_ex with
+ * {FVATTN_ROUTE_TOPP, p, k_min = 1, k_max = 0, window = 0}.
+ */
+int fvattn_route_ex(const void *q, const void *k, int B, int H, int N, int d, int dtype, int block_q,
+                    int block_k, const fvattn_route_opts *opts, fvattn_csr *csr, void *ws, size_t ws_bytes,
+                    void *stream);
 
 /*
  * Device-built work list (one-GPU analogue of the FVAttn summary's runtime load balancing:

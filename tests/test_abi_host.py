@@ -175,3 +175,29 @@ def test_product_never_touches_oracle():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 src = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"\boracle\b", src), f"{f} mentions the oracle"
+
+
+def _route_ex(L, opts, B=1, H=2, N=1024, d=64, dt=0, bq=64, bk=64, ws=FAKE, ws_bytes=1 << 40):
+    c = _csr(B * H, N, bq, bk)
+    return L.fvattn_route_ex(FAKE, FAKE, B, H, N, d, dt, bq, bk,
+                             ctypes.byref(opts) if opts is not None else None, ctypes.byref(c), ws, ws_bytes, None)
+
+
+def _ropts(mode=0, topk=0, p=0.9, k_min=1, k_max=0, window=0):
+    return fv._RouteOptsC(mode, topk, p, k_min, k_max, window, 0)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(mode=2), dict(mode=-1), dict(p=0.0), dict(p=1.5), dict(p=math.nan), dict(k_min=0),
+    dict(k_min=5, k_max=3), dict(k_max=-1), dict(mode=1, topk=0), dict(mode=1, topk=-3),
+    dict(window=-1), dict(mode=1, topk=4, window=-2),
+])
+def test_route_ex_rejects_bad_options(L, kw):
+    assert _route_ex(L, _ropts(**kw)) == INVALID
+
+
+def test_route_ex_validation_order(L):
+    assert _route_ex(L, None) == INVALID
+    assert _route_ex(L, _ropts(), d=96) == UNSUPPORTED           # shape checks as fvattn_route
+    assert _route_ex(L, _ropts(mode=1, topk=3), dt=5) == UNSUPPORTED
+    assert _route_ex(L, _ropts(mode=1, topk=3), ws_bytes=16) == WORKSPACE

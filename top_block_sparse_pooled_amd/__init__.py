@@ -23,6 +23,7 @@ LIB_PATH = os.path.join(_HERE, "libfvattn.so")
 
 BF16, F32 = 0, 1
 SCHED = {"lpt": 0, "identity": 1, "head_lpt": 2, "xcd": 3}
+ROUTE_MODES = {"topp": 0, "topk": 1}
 
 
 class FvAttnError(RuntimeError):
@@ -41,6 +42,12 @@ class _CsrC(ctypes.Structure):
 class _OptsC(ctypes.Structure):
     _fields_ = [("schedule", ctypes.c_int32), ("grid", ctypes.c_int32), ("trace", ctypes.c_void_p),
                 ("out_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class _RouteOptsC(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int32), ("topk", ctypes.c_int32), ("p", ctypes.c_double),
+                ("k_min", ctypes.c_int32), ("k_max", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 _LIB = None
@@ -68,6 +75,9 @@ def lib() -> ctypes.CDLL:
         L.fvattn_route.restype = i32
         L.fvattn_route.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32, dbl,
                                    ctypes.POINTER(_CsrC), vp, sz, vp]
+        L.fvattn_route_ex.restype = i32
+        L.fvattn_route_ex.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32, ctypes.POINTER(_RouteOptsC),
+                                      ctypes.POINTER(_CsrC), vp, sz, vp]
         L.fvattn_worklist.restype = i32
         L.fvattn_worklist.argtypes = [ctypes.POINTER(_CsrC), i32, vp, vp, vp]
         L.fvattn_attn_plan.restype = i32
@@ -202,8 +212,10 @@ def pool(x, block: int):
     return out
 
 
-def route(q, k, block_q: int, block_k: int, p: float, csr: Optional[Csr] = None, ws=None) -> Csr:
-    """Top-p routing -> Csr.  `csr` / `ws` may be preallocated (reused across calls)."""
+def route(q, k, block_q: int, block_k: int, p: float = 0.9, csr: Optional[Csr] = None, ws=None,
+          mode: str = "topp", topk: int = 0, k_min: int = 1, k_max: int = 0, window: int = 0) -> Csr:
+    """Top-p routing (or a variant: mode="topk" with topk, a [k_min, k_max] clamp of the
+    Top-p count, a local window) -> Csr.  `csr` / `ws` may be preallocated (reused)."""
     torch = _torch()
     _check_qkv(q, k)
     B, H, N, d = q.shape
@@ -213,9 +225,18 @@ def route(q, k, block_q: int, block_k: int, p: float, csr: Optional[Csr] = None,
     if ws is None:
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     c = csr.c()
-    _check(lib().fvattn_route(q.data_ptr(), k.data_ptr(), B, H, N, d, _dtype_code(q), block_q, block_k,
-                              float(p), ctypes.byref(c), ws.data_ptr(), ws.numel(), _stream(q.device)),
-           "fvattn_route")
+    if mode == "topp" and k_min == 1 and k_max == 0 and window == 0:
+        _check(lib().fvattn_route(q.data_ptr(), k.data_ptr(), B, H, N, d, _dtype_code(q), block_q, block_k,
+                                  float(p), ctypes.byref(c), ws.data_ptr(), ws.numel(), _stream(q.device)),
+               "fvattn_route")
+    else:
+        if mode not in ROUTE_MODES:
+            raise ValueError(f"mode must be one of {sorted(ROUTE_MODES)}")
+        o = _RouteOptsC(ROUTE_MODES[mode], int(topk), float(p), int(k_min), int(k_max), int(window), 0)
+        _check(lib().fvattn_route_ex(q.data_ptr(), k.data_ptr(), B, H, N, d, _dtype_code(q), block_q, block_k,
+                                     ctypes.byref(o), ctypes.byref(c), ws.data_ptr(), ws.numel(),
+                                     _stream(q.device)),
+               "fvattn_route_ex")
     csr.bh, csr.n, csr.block_q, csr.block_k, csr.nqb, csr.nkb = c.bh, c.n, c.block_q, c.block_k, c.nqb, c.nkb
     return csr
 

@@ -11,7 +11,8 @@ int launch_pool_qk(const void *q, const void *k, int BH, int N, int d, int dtype
                    double *qsw, double *ksw, int32_t *zero0, int nzero0, int32_t *zero1, int nzero1,
                    hipStream_t st);
 int launch_select(const double *qsw, const double *ksw, int BH, int d, int nqb, int nkb, double p,
-                  int32_t *counts, uint32_t *bitmask, int nkw, int32_t *head_load, int32_t *bsum, hipStream_t st);
+                  int32_t *counts, uint32_t *bitmask, int nkw, int32_t *head_load, int32_t *bsum, int mode, int topk,
+                  int k_min, int k_max, int window, int bq, int bk, int N, hipStream_t st);
 int launch_csr(const int32_t *counts, const uint32_t *bitmask, const int32_t *bsum, int rows, int nkw, int nkb,
                int32_t *row_ptr, int32_t *col_idx, hipStream_t st);
 int launch_vt(const void *v, void *vt, int BH, int N, int D, int NKP, hipStream_t st);
@@ -156,13 +157,24 @@ int fvattn_pool(const void *x, int BH, int N, int d, int dtype, int block, doubl
   return fv::launch_pool(x, BH, N, d, dtype, block, out, (hipStream_t)stream);
 }
 
-int fvattn_route(const void *q, const void *k, int B, int H, int N, int d, int dtype, int block_q, int block_k,
-                 double p, fvattn_csr *csr, void *ws, size_t ws_bytes, void *stream) {
+int fvattn_route_ex(const void *q, const void *k, int B, int H, int N, int d, int dtype, int block_q,
+                    int block_k, const fvattn_route_opts *opts, fvattn_csr *csr, void *ws, size_t ws_bytes,
+                    void *stream) {
   if (!dtype_ok(dtype)) return FVATTN_ERR_UNSUPPORTED;
+  if (opts == nullptr) return FVATTN_ERR_INVALID;
   Shape s;
   int rc = check_shape(B, H, N, d, block_q, block_k, &s);
   if (rc != FVATTN_OK) return rc;
-  if (!(p > 0.0 && p <= 1.0)) return FVATTN_ERR_INVALID;  // also rejects NaN
+  const fvattn_route_opts &o = *opts;
+  if (o.mode == FVATTN_ROUTE_TOPP) {
+    if (!(o.p > 0.0 && o.p <= 1.0)) return FVATTN_ERR_INVALID;  // also rejects NaN
+    if (o.k_min < 1 || o.k_max < 0 || (o.k_max > 0 && o.k_max < o.k_min)) return FVATTN_ERR_INVALID;
+  } else if (o.mode == FVATTN_ROUTE_TOPK) {
+    if (o.topk < 1) return FVATTN_ERR_INVALID;
+  } else {
+    return FVATTN_ERR_INVALID;
+  }
+  if (o.window < 0) return FVATTN_ERR_INVALID;
   if (q == nullptr || k == nullptr || csr == nullptr || ws == nullptr) return FVATTN_ERR_INVALID;
   if (csr->row_ptr == nullptr || csr->col_idx == nullptr || csr->head_load == nullptr) return FVATTN_ERR_INVALID;
   if (csr->capacity < (int64_t)s.rows * s.nkb) return FVATTN_ERR_CAPACITY;
@@ -174,10 +186,21 @@ int fvattn_route(const void *q, const void *k, int B, int H, int N, int d, int d
   if ((rc = fv::launch_pool_qk(q, k, s.BH, N, d, dtype, block_q, block_k, w.qsw, w.ksw, w.bsum, w.nblk,
                                csr->head_load, s.BH, st)) != FVATTN_OK)
     return rc;
+  const double p = o.mode == FVATTN_ROUTE_TOPP ? o.p : 1.0;
   if ((rc = fv::launch_select(w.qsw, w.ksw, s.BH, d, s.nqb, s.nkb, p, w.counts, w.bitmask, s.nkw, csr->head_load,
-                              w.bsum, st)) != FVATTN_OK)
+                              w.bsum, o.mode, o.topk, o.k_min, o.k_max, o.window, block_q, block_k, N, st)) !=
+      FVATTN_OK)
     return rc;
   return fv::launch_csr(w.counts, w.bitmask, w.bsum, s.rows, s.nkw, s.nkb, csr->row_ptr, csr->col_idx, st);
+}
+
+int fvattn_route(const void *q, const void *k, int B, int H, int N, int d, int dtype, int block_q, int block_k,
+                 double p, fvattn_csr *csr, void *ws, size_t ws_bytes, void *stream) {
+  fvattn_route_opts o{};
+  o.mode = FVATTN_ROUTE_TOPP;
+  o.p = p;
+  o.k_min = 1;
+  return fvattn_route_ex(q, k, B, H, N, d, dtype, block_q, block_k, &o, csr, ws, ws_bytes, stream);
 }
 
 int fvattn_worklist(const fvattn_csr *csr, int schedule, int32_t *worklist, int32_t *counter, void *stream) {

@@ -136,32 +136,44 @@ __global__ __launch_bounds__(256) void k_pool(PoolArgs a) {
 // ---------------------------------------------------------------------------------------
 constexpr int kMaxNkw = 40;  // 1280 key blocks
 
+// Routing variant of k_select (see fvattn_route_opts): mode, top-k count, clamp of the Top-p
+// count, local window, and the block geometry the window needs.
+struct SelOpts {
+  int mode, topk, k_min, k_max, window, bq, bk, N;
+};
+
 // Smallest shift with (width - 1) >> shift < 256: the digit of a key in a range of `width`.
 __device__ __forceinline__ int digit_shift(unsigned long long width) {
   const unsigned long long wm1 = width - 1ull;
   return wm1 < 256ull ? 0 : 64 - __clzll((long long)wm1) - 8;
 }
 
-template <int D, int MAXT>
-__global__ __launch_bounds__(256, MAXT <= 8 ? 2 : 1) void k_select(const double *__restrict__ qsw,
+// NWV waves per workgroup (4, or 8 for more than 512 key blocks): wave w holds key tiles
+// w, w + NWV, ... (MAXT of them).  EXT: routing variants (count searches, clamp, window).
+template <int D, int MAXT, int NWV, bool EXT>
+__global__ __launch_bounds__(64 * NWV, NWV == 4 ? 2 : 1) void k_select(const double *__restrict__ qsw,
                                                 const double *__restrict__ ksw, int nqb, int nkb,
                                                 double scale, double p, int32_t *__restrict__ counts,
                                                 uint32_t *__restrict__ bitmask, int nkw,
                                                 int32_t *__restrict__ head_load, int32_t *__restrict__ bsum,
-                                                int BH) {
+                                                int BH, SelOpts sel) {
   constexpr int KS = D / 4;  // MFMA k-steps
   __shared__ uint32_t h_cnt[16][256];
   __shared__ unsigned long long h_mass[16][256];
   __shared__ uint32_t s_kept[16][kMaxNkw];
   __shared__ uint32_t s_ties[16][kMaxNkw];
-  __shared__ double s_part[4][16];
-  __shared__ unsigned long long s_zpart[4][16];
+  __shared__ double s_part[NWV][16];
+  __shared__ unsigned long long s_zpart[NWV][16];
   __shared__ unsigned long long s_lo[16], s_width[16], s_above[16], s_target[16];
-  __shared__ double s_minpart[4][16];
-  __shared__ int s_state[16];   // 0 = searching, 1 = unique threshold found, 2 = ties, 3 = keep all
+  __shared__ double s_minpart[NWV][16];
+  __shared__ int s_state[16];   // 0 searching, 1 unique threshold, 2 ties, 3 keep all, 4 final
+  __shared__ int s_bycnt[16];   // search by count instead of mass
+  __shared__ unsigned long long s_lo0[16];
   __shared__ uint32_t s_selcnt[16];
   __shared__ int s_any;
 
+  constexpr int NT = 64 * NWV;      // threads
+  constexpr int RPW = 16 / NWV;     // rows resolved per wave
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int nqg = (nqb + 15) >> 4;
   const int nkt = (nkb + 15) >> 4;
@@ -187,7 +199,7 @@ __global__ __launch_bounds__(256, MAXT <= 8 ? 2 : 1) void k_select(const double 
     // valid tile (their key columns are >= nkb and ignored below), so the loop has no branches.
     const double *kb[MAXT];
 #pragma unroll
-    for (int k = 0; k < MAXT; ++k) kb[k] = ksw + ((size_t)(bh * nkt + min(w + 4 * k, nkt - 1)) * KS) * 64 + lane;
+    for (int k = 0; k < MAXT; ++k) kb[k] = ksw + ((size_t)(bh * nkt + min(w + NWV * k, nkt - 1)) * KS) * 64 + lane;
     double acur = qa[0], bcur[MAXT];
 #pragma unroll
     for (int k = 0; k < MAXT; ++k) bcur[k] = kb[k][0];
@@ -216,7 +228,7 @@ __global__ __launch_bounds__(256, MAXT <= 8 ? 2 : 1) void k_select(const double 
   for (int v = 0; v < 4; ++v) mx[v] = -INFINITY;
 #pragma unroll
   for (int k = 0; k < MAXT; ++k) {
-    const int j = 16 * (w + 4 * k) + jl;
+    const int j = 16 * (w + NWV * k) + jl;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       acc[k][v] *= scale;
@@ -233,7 +245,10 @@ __global__ __launch_bounds__(256, MAXT <= 8 ? 2 : 1) void k_select(const double 
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     const int r = ig + 4 * v;
-    mx[v] = fmax(fmax(s_part[0][r], s_part[1][r]), fmax(s_part[2][r], s_part[3][r]));
+    double m = s_part[0][r];
+#pragma unroll
+    for (int ww = 1; ww < NWV; ++ww) m = fmax(m, s_part[ww][r]);
+    mx[v] = m;
   }
 
   // ---- e = exp(s - max) (in place), fixed-point masses, Z
@@ -242,7 +257,7 @@ __global__ __launch_bounds__(256, MAXT <= 8 ? 2 : 1) void k_select(const double 
   double mn[4] = {1.0, 1.0, 1.0, 1.0};
 #pragma unroll
   for (int k = 0; k < MAXT; ++k) {
-    const int j = 16 * (w + 4 * k) + jl;
+    const int j = 16 * (w + NWV * k) + jl;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const double e = (j < nkb) ? exp(acc[k][v] - mx[v]) : 0.0;
@@ -264,38 +279,60 @@ __global__ __launch_bounds__(256, MAXT <= 8 ? 2 : 1) void k_select(const double 
     }
   }
   __syncthreads();
+  // ---- per-row selection setup.  A row searches by mass (Top-p: the shortest prefix of the
+  // descending order whose mass reaches p Z) or by count (top-k, or a clamped Top-p count):
+  // the same radix walk over mass or count histograms.
   if (tid < 16) {
     const int r = tid;
-    const unsigned long long Z = s_zpart[0][r] + s_zpart[1][r] + s_zpart[2][r] + s_zpart[3][r];
-    unsigned long long T = (unsigned long long)ceil(p * (double)Z);
-    if (T > Z) T = Z;
-    if (T < 1) T = 1;
-    s_target[r] = T;
+    unsigned long long Z = 0;
+    double emin = 1.0;
+    for (int ww = 0; ww < NWV; ++ww) {
+      Z += s_zpart[ww][r];
+      emin = fmin(emin, s_minpart[ww][r]);
+    }
     // search range of keys (float64 bit patterns of e, monotone for e >= 0): [e_min, 1.0]
-    const double emin = fmin(fmin(s_minpart[0][r], s_minpart[1][r]), fmin(s_minpart[2][r], s_minpart[3][r]));
     const unsigned long long lo = (unsigned long long)__double_as_longlong(emin);
+    const bool live = (16 * g + r) < nqb;
+    unsigned long long T;
+    int st;
+    if (EXT && sel.mode == FVATTN_ROUTE_TOPK) {
+      T = (unsigned long long)sel.topk;
+      st = (!live || sel.topk >= nkb) ? 3 : 0;
+      s_bycnt[r] = 1;
+    } else {
+      T = (unsigned long long)ceil(p * (double)Z);
+      if (T > Z) T = Z;
+      if (T < 1) T = 1;
+      st = (!live || p >= 1.0) ? 3 : 0;
+      s_bycnt[r] = 0;
+    }
+    s_target[r] = T;
+    s_lo0[r] = lo;
     s_lo[r] = lo;
     s_width[r] = (unsigned long long)__double_as_longlong(1.0) + 1ull - lo;
     s_above[r] = 0;
     s_selcnt[r] = 0;
-    const bool live = (16 * g + r) < nqb;
-    s_state[r] = (!live || p >= 1.0) ? 3 : 0;
+    s_state[r] = st;
   }
   __syncthreads();
 
-  // ---- radix select over the key range [lo, lo + width): each pass splits the range into
-  // 256 equal digit bins (log-linear in e), finds the bin where the cumulative mass from the
-  // top crosses the target, and narrows the range to that bin.  The first range spans the
-  // row's own [e_min, 1], so elements spread over the bins instead of piling into a few.
+  // Round 0 selects; with a clamp on the Top-p count, round 1 re-selects by count the rows
+  // whose kept count lies outside [k_min, k_max] (other rows are final: state 4).
+  const bool clamp = EXT && sel.mode != FVATTN_ROUTE_TOPK && (sel.k_min > 1 || sel.k_max > 0);
+  for (int round = 0; round < (EXT ? 2 : 1); ++round) {
+    // ---- radix select over the key range [lo, lo + width): each pass splits the range into
+    // 256 equal digit bins (log-linear in e), finds the bin where the cumulative mass (or
+    // count) from the top crosses the target, and narrows the range to that bin.  The first
+    // range spans the row's own [e_min, 1], so elements spread over the bins.
   for (int pass = 0; pass < 8; ++pass) {
     if (tid == 0) {
       int any = 0;
       for (int r = 0; r < 16; ++r) any |= (s_state[r] == 0);
       s_any = any;
     }
-    for (int r = 0; r < 16; ++r) {
-      h_cnt[r][tid] = 0;
-      h_mass[r][tid] = 0;
+    for (int i = tid; i < 16 * 256; i += NT) {
+      (&h_cnt[0][0])[i] = 0;
+      (&h_mass[0][0])[i] = 0;
     }
     __syncthreads();
     if (!s_any) break;
@@ -312,7 +349,7 @@ __global__ __launch_bounds__(256, MAXT <= 8 ? 2 : 1) void k_select(const double 
     }
 #pragma unroll
     for (int k = 0; k < MAXT; ++k) {
-      const int j = 16 * (w + 4 * k) + jl;
+      const int j = 16 * (w + NWV * k) + jl;
       if (j < nkb) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
@@ -328,16 +365,18 @@ __global__ __launch_bounds__(256, MAXT <= 8 ? 2 : 1) void k_select(const double 
     }
     __syncthreads();
     // wave w resolves rows 4w .. 4w+3: find the digit where the mass crosses the target
-    for (int rr = 0; rr < 4; ++rr) {
-      const int r = 4 * w + rr;
+    for (int rr = 0; rr < RPW; ++rr) {
+      const int r = RPW * w + rr;
       if (s_state[r] != 0) continue;  // uniform across the wave
+      // the walk runs over masses (Top-p) or counts (top-k, clamped count)
+      const bool bc = EXT && s_bycnt[r] != 0;
       unsigned long long m4[4];
       uint32_t c4[4];
       unsigned long long ms = 0;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        m4[q] = h_mass[r][4 * lane + q];
         c4[q] = h_cnt[r][4 * lane + q];
+        m4[q] = bc ? (unsigned long long)c4[q] : h_mass[r][4 * lane + q];
         ms += m4[q];
       }
       // exclusive suffix sums over lanes (higher lanes hold larger digits)
@@ -369,19 +408,21 @@ __global__ __launch_bounds__(256, MAXT <= 8 ? 2 : 1) void k_select(const double 
   }
 
   // ---- mark kept blocks
-  for (int i = tid; i < 16 * kMaxNkw; i += 256) {
+  for (int i = tid; i < 16 * kMaxNkw; i += NT) {
+    if (s_state[i / kMaxNkw] == 4) continue;   // final from the previous round
     (&s_kept[0][0])[i] = 0;
     (&s_ties[0][0])[i] = 0;
   }
   __syncthreads();
 #pragma unroll
   for (int k = 0; k < MAXT; ++k) {
-    const int j = 16 * (w + 4 * k) + jl;
+    const int j = 16 * (w + NWV * k) + jl;
     if (j < nkb) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int r = ig + 4 * v;
         const int st = s_state[r];
+        if (st == 4) continue;
         const unsigned long long key = (unsigned long long)__double_as_longlong(acc[k][v]);
         const unsigned long long lo = s_lo[r], hi = lo + s_width[r];
         const uint32_t bit = 1u << (j & 31);
@@ -399,7 +440,7 @@ __global__ __launch_bounds__(256, MAXT <= 8 ? 2 : 1) void k_select(const double 
   __shared__ unsigned long long s_mt[16];
 #pragma unroll
   for (int k = 0; k < MAXT; ++k) {
-    const int j = 16 * (w + 4 * k) + jl;
+    const int j = 16 * (w + NWV * k) + jl;
     if (j < nkb) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
@@ -410,13 +451,17 @@ __global__ __launch_bounds__(256, MAXT <= 8 ? 2 : 1) void k_select(const double 
     }
   }
   __syncthreads();
-  for (int rr = 0; rr < 4; ++rr) {
-    const int r = 4 * w + rr;
+  for (int rr = 0; rr < RPW; ++rr) {
+    const int r = RPW * w + rr;
     if (s_state[r] != 2) continue;
     const unsigned long long rem = s_target[r] - s_above[r];
     const unsigned long long mt = s_mt[r];
     const uint32_t ntie = s_selcnt[r];
-    uint32_t need = (mt == 0) ? ntie : (uint32_t)min((unsigned long long)ntie, (rem + mt - 1) / mt);
+    uint32_t need;
+    if (EXT && s_bycnt[r])
+      need = (uint32_t)min((unsigned long long)ntie, rem);   // count search: rem blocks
+    else
+      need = (mt == 0) ? ntie : (uint32_t)min((unsigned long long)ntie, (rem + mt - 1) / mt);
     uint32_t word = lane < nkw ? s_ties[r][lane] : 0u;
     const uint32_t pc = __popc(word);
     uint32_t incl = pc;
@@ -440,13 +485,60 @@ __global__ __launch_bounds__(256, MAXT <= 8 ? 2 : 1) void k_select(const double 
   }
   __syncthreads();
 
+
+  if constexpr (EXT) {
+  if (!clamp || round == 1) break;
+  for (int rr = 0; rr < RPW; ++rr) {
+    const int r = RPW * w + rr;
+    uint32_t word = lane < nkw ? s_kept[r][lane] : 0u;
+    int c = __popc(word);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) c += __shfl_xor(c, off);
+    if (lane == 0) {
+      int tgt = max(c, sel.k_min);
+      if (sel.k_max > 0) tgt = min(tgt, sel.k_max);
+      tgt = min(tgt, nkb);
+      if ((16 * g + r) < nqb && tgt != c) {
+        s_bycnt[r] = 1;
+        s_target[r] = (unsigned long long)tgt;
+        s_lo[r] = s_lo0[r];
+        s_width[r] = (unsigned long long)__double_as_longlong(1.0) + 1ull - s_lo0[r];
+        s_above[r] = 0;
+        s_selcnt[r] = 0;
+        s_state[r] = tgt >= nkb ? 3 : 0;
+      } else {
+        s_state[r] = 4;
+      }
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int any = 0;
+    for (int r = 0; r < 16; ++r) any |= (s_state[r] != 4);
+    s_any = any;
+  }
+  __syncthreads();
+  if (!s_any) break;
+  }
+  }   // rounds
+
   // ---- write counts, masks, loads (wave w: rows 4w..4w+3)
-  for (int rr = 0; rr < 4; ++rr) {
-    const int r = 4 * w + rr;
+  for (int rr = 0; rr < RPW; ++rr) {
+    const int r = RPW * w + rr;
     const int i = 16 * g + r;
     if (i >= nqb) continue;
     const size_t row = (size_t)bh * nqb + i;
     uint32_t word = lane < nkw ? s_kept[r][lane] : 0u;
+    if (EXT && sel.window > 0 && lane < nkw) {
+      // local window: key blocks within `window` of those overlapping the query block's tokens
+      const int t0 = i * sel.bq, t1 = min(t0 + sel.bq, sel.N) - 1;
+      const int ja = max(0, t0 / sel.bk - sel.window), jb = min(nkb - 1, t1 / sel.bk + sel.window);
+      const int lo_j = max(ja, 32 * lane), hi_j = min(jb, 32 * lane + 31);
+      if (lo_j <= hi_j) {
+        const int nbits = hi_j - lo_j + 1;
+        word |= (nbits == 32 ? 0xffffffffu : ((1u << nbits) - 1u)) << (lo_j - 32 * lane);
+      }
+    }
     if (lane < nkw) bitmask[row * nkw + lane] = word;
     int c = __popc(word);
 #pragma unroll
@@ -565,45 +657,50 @@ int launch_pool_qk(const void *q, const void *k, int BH, int N, int d, int dtype
   return launch_pool_args(pa, BH, d, dtype, st);
 }
 
-template <int D, int MT>
+template <int D, int MT, int NWV>
 static int launch_select_mt(const double *qsw, const double *ksw, int BH, int nqb, int nkb, double p,
                             int32_t *counts, uint32_t *bitmask, int nkw, int32_t *head_load, int32_t *bsum,
-                            hipStream_t st) {
-  auto kern = k_select<D, MT>;
+                            const SelOpts &sel, hipStream_t st) {
+  auto kern = (sel.mode != FVATTN_ROUTE_TOPP || sel.k_min > 1 || sel.k_max > 0 || sel.window > 0)
+                  ? k_select<D, MT, NWV, true>
+                  : k_select<D, MT, NWV, false>;
   int cus = 0, occ = 0;
   if (device_cus(&cus) != 0) return FVATTN_ERR_HIP;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, 256, 0) != hipSuccess) return FVATTN_ERR_HIP;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, 64 * NWV, 0) != hipSuccess) return FVATTN_ERR_HIP;
   const int items = cdiv(nqb, 16) * BH;
   int grid = cus * (occ > 0 ? occ : 1);
   if (grid > items) grid = items;
   if (grid < 8) grid = 8;   // every XCD range needs a worker
   const double scale = 1.0 / sqrt((double)D);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, st, qsw, ksw, nqb, nkb, scale, p, counts, bitmask, nkw,
-                     head_load, bsum, BH);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * NWV), 0, st, qsw, ksw, nqb, nkb, scale, p, counts, bitmask, nkw,
+                     head_load, bsum, BH, sel);
   FV_CHECK_LAUNCH();
   return FVATTN_OK;
 }
 
+// Key tiles (of 16 blocks) per wave: up to 512 key blocks run on 4 waves with at most 8 tiles
+// each; more (up to 1280) on 8 waves with at most 10 tiles each.
 template <int D>
 static int launch_select_d(const double *qsw, const double *ksw, int BH, int nqb, int nkb, double p,
                            int32_t *counts, uint32_t *bitmask, int nkw, int32_t *head_load, int32_t *bsum,
-                           hipStream_t st) {
-  const int per_wave = cdiv(cdiv(nkb, 16), 4);
-#define FV_SEL(MT) \
-  return launch_select_mt<D, MT>(qsw, ksw, BH, nqb, nkb, p, counts, bitmask, nkw, head_load, bsum, st)
-  if (per_wave <= 1) FV_SEL(1);
-  if (per_wave <= 2) FV_SEL(2);
-  if (per_wave <= 4) FV_SEL(4);
-  if (per_wave <= 8) FV_SEL(8);
-  if (per_wave <= 12) FV_SEL(12);
-  FV_SEL(20);
+                           const SelOpts &sel, hipStream_t st) {
+  const int nkt = cdiv(nkb, 16);
+#define FV_SEL(MT, NWV) \
+  return launch_select_mt<D, MT, NWV>(qsw, ksw, BH, nqb, nkb, p, counts, bitmask, nkw, head_load, bsum, sel, st)
+  if (nkt <= 4) FV_SEL(1, 4);
+  if (nkt <= 8) FV_SEL(2, 4);
+  if (nkt <= 16) FV_SEL(4, 4);
+  if (nkt <= 32) FV_SEL(8, 4);
+  FV_SEL(10, 8);
 #undef FV_SEL
 }
 
 int launch_select(const double *qsw, const double *ksw, int BH, int d, int nqb, int nkb, double p,
-                  int32_t *counts, uint32_t *bitmask, int nkw, int32_t *head_load, int32_t *bsum, hipStream_t st) {
-  if (d == 128) return launch_select_d<128>(qsw, ksw, BH, nqb, nkb, p, counts, bitmask, nkw, head_load, bsum, st);
-  return launch_select_d<64>(qsw, ksw, BH, nqb, nkb, p, counts, bitmask, nkw, head_load, bsum, st);
+                  int32_t *counts, uint32_t *bitmask, int nkw, int32_t *head_load, int32_t *bsum, int mode, int topk,
+                  int k_min, int k_max, int window, int bq, int bk, int N, hipStream_t st) {
+  const SelOpts sel{mode, topk, k_min, k_max, window, bq, bk, N};
+  if (d == 128) return launch_select_d<128>(qsw, ksw, BH, nqb, nkb, p, counts, bitmask, nkw, head_load, bsum, sel, st);
+  return launch_select_d<64>(qsw, ksw, BH, nqb, nkb, p, counts, bitmask, nkw, head_load, bsum, sel, st);
 }
 
 int launch_csr(const int32_t *counts, const uint32_t *bitmask, const int32_t *bsum, int rows, int nkw, int nkb,
