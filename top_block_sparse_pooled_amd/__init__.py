@@ -54,11 +54,11 @@ _LIB = None
 
 
 def lib() -> ctypes.CDLL:
-    """Load libfvattn.so (built in-tree by __graft_entry__.build / _build.py)."""
+    """Load libfvattn.so (built in-tree by __graft_entry__.build / hipbuild.py)."""
     global _LIB
     if _LIB is None:
         if not os.path.exists(LIB_PATH):
-            raise ImportError(f"{LIB_PATH} is not built; run `python -m top_block_sparse_pooled_amd._build`")
+            raise ImportError(f"{LIB_PATH} is not built; run `python -m top_block_sparse_pooled_amd.hipbuild`")
         L = ctypes.CDLL(LIB_PATH)
         i32, i64, vp, sz, dbl = ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_double
         L.fvattn_version.restype = i32

@@ -1,6 +1,6 @@
 """Build libfvattn.so in-tree with hipcc for gfx950.
 
-    python -m top_block_sparse_pooled_amd._build
+    python -m top_block_sparse_pooled_amd.hipbuild
 """
 from __future__ import annotations
 
