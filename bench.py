@@ -118,11 +118,16 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip trace/copy-bandwidth extras (profiling runs)")
+    ap.add_argument("--mode", default="topp", choices=["topp", "topk"], help="routing variant (default Top-p)")
+    ap.add_argument("--topk", type=int, default=0, help="blocks per row for --mode topk")
+    ap.add_argument("--k-min", type=int, default=1, help="lower clamp of the Top-p count")
+    ap.add_argument("--k-max", type=int, default=0, help="upper clamp of the Top-p count (0: none)")
+    ap.add_argument("--window", type=int, default=0, help="local window of key blocks kept around each query block")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps(dict(error="this build runs on one GPU only: the hot path is measured on one GPU's "
+        print(json.dumps(dict(error="this benchmark runs on one GPU: the hot path is measured on one GPU's "
                                     "share; multi-GPU runs are not supported", n_gpus=args.gpus)))
         sys.exit(2)
 
@@ -148,10 +153,14 @@ def main():
     aws = fv.attn_ws(qd, csr)
     o = torch.empty(qd.shape, dtype=out_dtype or tdt, device=dev)
 
+    variant = dict(mode=args.mode, topk=args.topk, k_min=args.k_min, k_max=args.k_max, window=args.window)
+    if args.mode == "topk" and args.topk < 1:
+        raise SystemExit("--mode topk needs --topk >= 1")
+
     def step(ev=None):
         if ev is not None:
             ev[0].record()
-        fv.route(qd, kd, w.block_q, w.block_k, p, csr=csr, ws=rws)
+        fv.route(qd, kd, w.block_q, w.block_k, p, csr=csr, ws=rws, **variant)
         if ev is not None:
             ev[1].record()
         fv.attn_plan(vd, csr, aws, args.schedule)
@@ -195,7 +204,10 @@ def main():
     if os.path.exists(prof):
         try:
             pc = json.load(open(prof))
-            if pc.get("kernel_source_sha") == _attn_source_sha():
+            same = (pc.get("kernel_source_sha") == _attn_source_sha() and pc.get("p") == p
+                    and pc.get("schedule") == args.schedule and pc.get("routing", "topp") == "topp"
+                    and args.mode == "topp" and args.k_min == 1 and args.k_max == 0 and args.window == 0)
+            if same:
                 traffic = pc.get("bytes_per_launch")
         except Exception:
             traffic = None
@@ -247,6 +259,8 @@ def main():
         ms_per_step=ms_step, higher_is_better=True, scaling="weak", vs_baseline=None, dtype=w.dtype,
         data="synthetic",
         config=dict(workload=w.name, B=1, H=w.H, N=w.N, d=w.d, block_q=w.block_q, block_k=w.block_k, p=p,
+                    routing=(variant if (args.mode != "topp" or args.k_min != 1 or args.k_max or args.window)
+                             else "topp"),
                     schedule=args.schedule, out=args.out, nnz=nnz, kept_frac=nnz / (w.rows * w.nkb),
                     executed_tflop=flops / 1e12, nominal_tflop=flops_nominal / 1e12),
         stages_ms=dict(route=route_ms, plan=plan_ms, attn=attn_ms),
