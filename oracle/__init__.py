@@ -7,5 +7,6 @@ to it, and it imports nothing from the GPU path.
 from .topp_oracle import (  # noqa: F401
     block_bounds, pool_blocks, block_scores, block_importance, routing_order,
     topp_count, route_head, route, sparse_attention_rows, sparse_attention,
-    dense_attention, lpt_worklist, csr_rows, selection_count, window_blocks,
+    dense_attention, lpt_worklist, csr_rows, selection_count, window_blocks, sasa_augment,
+    route_sasa, sasa_budget,
 )

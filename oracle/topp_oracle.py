@@ -263,3 +263,78 @@ def dense_attention(q, k, v) -> np.ndarray:
 def lpt_worklist(row_ptr: np.ndarray) -> np.ndarray:
     counts = np.diff(np.asarray(row_ptr, dtype=np.int64))
     return np.argsort(-counts, kind="stable").astype(np.int64)
+
+
+# --------------------------------------------------------------------------
+# SASA, slack-aware sparsity augmentation ([FVAttn] SASA section).  After load
+# balancing every rank knows its own block count and the largest one (the
+# critical path); the difference is its slack.  A rank adds the highest-
+# importance blocks that Top-p left out, taken from the candidate lists of all
+# its heads in the routing's importance order, as many as its slack allows,
+# scaled by an augmentation coefficient, and only when the slack passes a
+# trigger threshold.  Readings for one GPU:
+#   * ranks are R contiguous groups of the layer's heads (the per-rank share of
+#     sequence parallelism); the critical path is the largest group load, or a
+#     caller-given value (e.g. gathered from the other ranks);
+#   * load = kept (query block, key block) pairs; slack = critical - load;
+#     budget = floor(alpha * slack) if slack >= tau * critical and slack > 0,
+#     else 0;
+#   * candidates = every unselected (row, key block) of the group's rows,
+#     ranked by importance P descending, ties to the lower row, then the lower
+#     key block; the first `budget` are added.
+# --------------------------------------------------------------------------
+def sasa_budget(slack: int, critical: int, alpha: float, tau: float) -> int:
+    """Blocks a group may add: floor(alpha * slack) when the slack passes the trigger."""
+    if slack <= 0 or slack < tau * critical:
+        return 0
+    return int(math.floor(alpha * slack))
+
+
+def sasa_augment(kept_per_head, P_per_head, groups: int, alpha: float, tau: float,
+                 critical: int = 0):
+    """kept_per_head[h][i]: ascending kept key blocks; P_per_head[h]: importance
+    [nqb, nkb].  Returns (augmented kept lists, per-group budgets, critical path)."""
+    H = len(kept_per_head)
+    nqb, nkb = P_per_head[0].shape
+    group_of = [h * groups // H for h in range(H)]
+    loads = [sum(len(x) for x in kept_per_head[h]) for h in range(H)]
+    L = [sum(loads[h] for h in range(H) if group_of[h] == g) for g in range(groups)]
+    crit = int(critical) if critical > 0 else max(L)
+    out = [[np.asarray(x, dtype=np.int64) for x in head] for head in kept_per_head]
+    budgets = []
+    for g in range(groups):
+        slack = crit - L[g]
+        budget = sasa_budget(slack, crit, alpha, tau)
+        budgets.append(budget)
+        if budget <= 0:
+            continue
+        cands = []
+        for h in range(H):
+            if group_of[h] != g:
+                continue
+            for i in range(nqb):
+                keep = np.zeros(nkb, dtype=bool)
+                keep[kept_per_head[h][i]] = True
+                for j in np.nonzero(~keep)[0]:
+                    cands.append((-P_per_head[h][i, j], h * nqb + i, int(j)))
+        cands.sort()
+        for _, row, j in cands[:budget]:
+            h, i = divmod(row, nqb)
+            out[h][i] = np.union1d(out[h][i], [j]).astype(np.int64)
+    return out, budgets, crit
+
+
+def route_sasa(q, k, block_q: int, block_k: int, p: float, groups: int, alpha: float, tau: float,
+               critical: int = 0, **variant):
+    """Routing (Top-p or a variant) followed by SASA over the heads of B x H."""
+    B, H, N, d = q.shape
+    kept_all, P_all = [], []
+    for b in range(B):
+        for h in range(H):
+            kept, extra = route_head(q[b, h], k[b, h], block_q, block_k, p, True, **variant)
+            kept_all.append(kept)
+            P_all.append(extra["P"])
+    aug, budgets, crit = sasa_augment(kept_all, P_all, groups, alpha, tau, critical)
+    row_ptr, col_idx, head_load = csr_rows(aug)
+    return dict(row_ptr=row_ptr, col_idx=col_idx, head_load=head_load, nnz=int(row_ptr[-1]),
+                kept=aug, base_kept=kept_all, P=P_all, budgets=budgets, critical=crit)
