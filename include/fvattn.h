@@ -188,6 +188,44 @@ int fvattn_route_ex(const void *q, const void *k, int B, int H, int N, int d, in
                     void *stream);
 
 /*
+ * Options of fvattn_route_sasa: SASA, slack-aware sparsity augmentation (FVAttn summary,
+ * SASA section).  After load balancing every rank knows its kept-block count and the largest
+ * one (the critical path); a rank with slack adds the highest-importance blocks that the
+ * routing left out, from the candidates of all its heads, within its slack scaled by an
+ * augmentation coefficient, and only when the slack passes a trigger threshold.  On one GPU
+ * a rank is one of `groups` contiguous groups of the B*H heads (head h is in group
+ * h*groups/(B*H)), the per-rank share of sequence parallelism.
+ *   groups    1 .. min(B*H, 1024)
+ *   critical  > 0: the critical path in kept blocks (for example the largest rank load
+ *             gathered from the other ranks); 0: the largest group load
+ *   alpha     augmentation coefficient in [0, 1]: a group adds floor(alpha * slack) blocks
+ *   tau       trigger threshold in [0, 1]: only groups with slack >= tau * critical add blocks
+ *   added     optional device int32[groups]: blocks added per group (NULL: not written)
+ * Candidates of a group: its rows' unselected (row, key block) pairs, ordered by importance
+ * (the routing's softmax over key blocks) descending, then row, then key block ascending.
+ */
+typedef struct fvattn_sasa_opts {
+  int32_t groups;
+  int32_t critical;
+  double alpha;
+  double tau;
+  int32_t *added;
+} fvattn_sasa_opts;
+
+/* Bytes of workspace fvattn_route_sasa needs (0 on invalid arguments). */
+size_t fvattn_route_sasa_ws_bytes(int B, int H, int N, int d, int block_q, int block_k, int groups);
+
+/*
+ * Routing (as fvattn_route_ex with ropts) followed by SASA (sopts); the CSR and head_load
+ * hold the augmented kept sets.  Workspace: fvattn_route_sasa_ws_bytes(...) bytes.  Errors as
+ * fvattn_route_ex; invalid SASA options return FVATTN_ERR_INVALID.  A group's augmented load
+ * never exceeds the critical path.
+ */
+int fvattn_route_sasa(const void *q, const void *k, int B, int H, int N, int d, int dtype, int block_q,
+                      int block_k, const fvattn_route_opts *ropts, const fvattn_sasa_opts *sopts,
+                      fvattn_csr *csr, void *ws, size_t ws_bytes, void *stream);
+
+/*
  * Device-built work list (one-GPU analogue of the FVAttn summary's runtime load balancing:
  * the heaviest work is placed first).  worklist: device int32 [rows] receives a permutation
  * of the rows in the requested FVATTN_SCHED_* order.  counter (optional, may be NULL):

@@ -293,7 +293,7 @@ def sasa_budget(slack: int, critical: int, alpha: float, tau: float) -> int:
 def sasa_augment(kept_per_head, P_per_head, groups: int, alpha: float, tau: float,
                  critical: int = 0):
     """kept_per_head[h][i]: ascending kept key blocks; P_per_head[h]: importance
-    [nqb, nkb].  Returns (augmented kept lists, per-group budgets, critical path)."""
+    [nqb, nkb].  Returns (augmented kept lists, per-group blocks added, critical path)."""
     H = len(kept_per_head)
     nqb, nkb = P_per_head[0].shape
     group_of = [h * groups // H for h in range(H)]
@@ -305,8 +305,8 @@ def sasa_augment(kept_per_head, P_per_head, groups: int, alpha: float, tau: floa
     for g in range(groups):
         slack = crit - L[g]
         budget = sasa_budget(slack, crit, alpha, tau)
-        budgets.append(budget)
         if budget <= 0:
+            budgets.append(0)
             continue
         cands = []
         for h in range(H):
@@ -318,6 +318,8 @@ def sasa_augment(kept_per_head, P_per_head, groups: int, alpha: float, tau: floa
                 for j in np.nonzero(~keep)[0]:
                     cands.append((-P_per_head[h][i, j], h * nqb + i, int(j)))
         cands.sort()
+        budget = min(budget, len(cands))      # a group cannot add more blocks than it left out
+        budgets.append(budget)
         for _, row, j in cands[:budget]:
             h, i = divmod(row, nqb)
             out[h][i] = np.union1d(out[h][i], [j]).astype(np.int64)

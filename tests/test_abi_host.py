@@ -201,3 +201,30 @@ def test_route_ex_validation_order(L):
     assert _route_ex(L, _ropts(), d=96) == UNSUPPORTED           # shape checks as fvattn_route
     assert _route_ex(L, _ropts(mode=1, topk=3), dt=5) == UNSUPPORTED
     assert _route_ex(L, _ropts(mode=1, topk=3), ws_bytes=16) == WORKSPACE
+
+
+def _sopts(groups=2, critical=0, alpha=0.5, tau=0.0):
+    return fv._SasaOptsC(groups, critical, alpha, tau, None)
+
+
+def _route_sasa(L, so, ro=None, B=1, H=2, N=1024, d=64, bq=64, bk=64, ws_bytes=1 << 40):
+    c = _csr(B * H, N, bq, bk)
+    ro = ro if ro is not None else _ropts()
+    return L.fvattn_route_sasa(FAKE, FAKE, B, H, N, d, 0, bq, bk, ctypes.byref(ro),
+                               ctypes.byref(so) if so is not None else None, ctypes.byref(c), FAKE, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw", [dict(groups=0), dict(groups=3), dict(alpha=-0.1), dict(alpha=1.5),
+                                dict(alpha=math.nan), dict(tau=-1.0), dict(tau=2.0), dict(critical=-5)])
+def test_route_sasa_rejects_bad_options(L, kw):
+    assert _route_sasa(L, _sopts(**kw)) == INVALID     # groups=3 > B*H=2
+
+
+def test_route_sasa_validation_order(L):
+    assert _route_sasa(L, None) == INVALID
+    assert _route_sasa(L, _sopts(), ro=_ropts(p=2.0)) == INVALID
+    assert _route_sasa(L, _sopts(), d=96) == UNSUPPORTED
+    need = L.fvattn_route_sasa_ws_bytes(1, 2, 1024, 64, 64, 64, 2)
+    assert need > L.fvattn_route_ws_bytes(1, 2, 1024, 64, 64, 64) + 2 * 16 * 16 * 8
+    assert L.fvattn_route_sasa_ws_bytes(1, 2, 1024, 64, 64, 64, 3) == 0
+    assert _route_sasa(L, _sopts(), ws_bytes=need - 1) == WORKSPACE

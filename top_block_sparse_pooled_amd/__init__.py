@@ -50,6 +50,11 @@ class _RouteOptsC(ctypes.Structure):
                 ("reserved", ctypes.c_int32)]
 
 
+class _SasaOptsC(ctypes.Structure):
+    _fields_ = [("groups", ctypes.c_int32), ("critical", ctypes.c_int32), ("alpha", ctypes.c_double),
+                ("tau", ctypes.c_double), ("added", ctypes.c_void_p)]
+
+
 _LIB = None
 
 
@@ -78,6 +83,11 @@ def lib() -> ctypes.CDLL:
         L.fvattn_route_ex.restype = i32
         L.fvattn_route_ex.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32, ctypes.POINTER(_RouteOptsC),
                                       ctypes.POINTER(_CsrC), vp, sz, vp]
+        L.fvattn_route_sasa_ws_bytes.restype = sz
+        L.fvattn_route_sasa_ws_bytes.argtypes = [i32] * 7
+        L.fvattn_route_sasa.restype = i32
+        L.fvattn_route_sasa.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32, ctypes.POINTER(_RouteOptsC),
+                                        ctypes.POINTER(_SasaOptsC), ctypes.POINTER(_CsrC), vp, sz, vp]
         L.fvattn_worklist.restype = i32
         L.fvattn_worklist.argtypes = [ctypes.POINTER(_CsrC), i32, vp, vp, vp]
         L.fvattn_attn_plan.restype = i32
@@ -237,6 +247,38 @@ def route(q, k, block_q: int, block_k: int, p: float = 0.9, csr: Optional[Csr] =
                                      ctypes.byref(o), ctypes.byref(c), ws.data_ptr(), ws.numel(),
                                      _stream(q.device)),
                "fvattn_route_ex")
+    csr.bh, csr.n, csr.block_q, csr.block_k, csr.nqb, csr.nkb = c.bh, c.n, c.block_q, c.block_k, c.nqb, c.nkb
+    return csr
+
+
+def route_sasa(q, k, block_q: int, block_k: int, p: float = 0.9, groups: int = 8, alpha: float = 0.5,
+               tau: float = 0.0, critical: int = 0, csr: Optional[Csr] = None, ws=None, added=None,
+               mode: str = "topp", topk: int = 0, k_min: int = 1, k_max: int = 0, window: int = 0) -> Csr:
+    """Routing (Top-p or a variant) followed by SASA over `groups` contiguous head groups ->
+    Csr of the augmented kept sets.  `added` (optional int32 tensor [groups]) receives the
+    blocks added per group."""
+    torch = _torch()
+    _check_qkv(q, k)
+    B, H, N, d = q.shape
+    if mode not in ROUTE_MODES:
+        raise ValueError(f"mode must be one of {sorted(ROUTE_MODES)}")
+    if csr is None:
+        csr = Csr.empty(B, H, N, block_q, block_k, q.device)
+    need = lib().fvattn_route_sasa_ws_bytes(B, H, N, d, block_q, block_k, int(groups))
+    if need == 0:
+        raise ValueError("invalid shape or group count for SASA")
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if added is not None and (added.dtype != torch.int32 or added.numel() < groups or not added.is_cuda):
+        raise ValueError("added must be a CUDA int32 tensor with at least `groups` elements")
+    ro = _RouteOptsC(ROUTE_MODES[mode], int(topk), float(p), int(k_min), int(k_max), int(window), 0)
+    so = _SasaOptsC(int(groups), int(critical), float(alpha), float(tau),
+                    added.data_ptr() if added is not None else None)
+    c = csr.c()
+    _check(lib().fvattn_route_sasa(q.data_ptr(), k.data_ptr(), B, H, N, d, _dtype_code(q), block_q, block_k,
+                                   ctypes.byref(ro), ctypes.byref(so), ctypes.byref(c), ws.data_ptr(), ws.numel(),
+                                   _stream(q.device)),
+           "fvattn_route_sasa")
     csr.bh, csr.n, csr.block_q, csr.block_k, csr.nqb, csr.nkb = c.bh, c.n, c.block_q, c.block_k, c.nqb, c.nkb
     return csr
 

@@ -10,9 +10,13 @@ int launch_pool(const void *x, int BH, int N, int d, int dtype, int block, doubl
 int launch_pool_qk(const void *q, const void *k, int BH, int N, int d, int dtype, int block_q, int block_k,
                    double *qsw, double *ksw, int32_t *zero0, int nzero0, int32_t *zero1, int nzero1,
                    hipStream_t st);
+size_t sasa_group_bytes(int R);
+int launch_sasa(const double *imp, uint32_t *bitmask, int32_t *counts, int32_t *bsum, int32_t *head_load, int nkw,
+                int nqb, int nkb, int BH, int R, int critical, double alpha, double tau, void *grp_buf,
+                uint32_t *ghist, int32_t *tiecnt, int32_t *tiepre, int32_t *added_out, hipStream_t st);
 int launch_select(const double *qsw, const double *ksw, int BH, int d, int nqb, int nkb, double p,
                   int32_t *counts, uint32_t *bitmask, int nkw, int32_t *head_load, int32_t *bsum, int mode, int topk,
-                  int k_min, int k_max, int window, int bq, int bk, int N, hipStream_t st);
+                  int k_min, int k_max, int window, int bq, int bk, int N, double *imp, hipStream_t st);
 int launch_csr(const int32_t *counts, const uint32_t *bitmask, const int32_t *bsum, int rows, int nkw, int nkb,
                int32_t *row_ptr, int32_t *col_idx, hipStream_t st);
 int launch_vt(const void *v, void *vt, int BH, int N, int D, int NKP, hipStream_t st);
@@ -80,6 +84,33 @@ RouteWs route_ws_layout(const Shape &s, char *base) {
   w.nblk = (s.rows + 63) / 64;
   w.bsum = (int32_t *)(base + off);
   off += align256((size_t)w.nblk * sizeof(int32_t));
+  w.bytes = off;
+  return w;
+}
+
+// SASA workspace, after the routing workspace: importance of every block, per-group state,
+// per-group histograms, per-row tie counts and running ranks.
+struct SasaWs {
+  double *imp;
+  void *grp;
+  uint32_t *ghist;
+  int32_t *tiecnt, *tiepre;
+  size_t bytes;   // including the routing workspace
+};
+
+SasaWs sasa_ws_layout(const Shape &s, int R, char *base) {
+  SasaWs w;
+  size_t off = align256(route_ws_layout(s, nullptr).bytes);
+  w.imp = (double *)(base + off);
+  off += align256((size_t)s.rows * s.nkb * sizeof(double));
+  w.grp = base + off;
+  off += align256(fv::sasa_group_bytes(R));
+  w.ghist = (uint32_t *)(base + off);
+  off += align256((size_t)R * 256 * sizeof(uint32_t));
+  w.tiecnt = (int32_t *)(base + off);
+  off += align256((size_t)s.rows * sizeof(int32_t));
+  w.tiepre = (int32_t *)(base + off);
+  off += align256((size_t)s.rows * sizeof(int32_t));
   w.bytes = off;
   return w;
 }
@@ -157,15 +188,9 @@ int fvattn_pool(const void *x, int BH, int N, int d, int dtype, int block, doubl
   return fv::launch_pool(x, BH, N, d, dtype, block, out, (hipStream_t)stream);
 }
 
-int fvattn_route_ex(const void *q, const void *k, int B, int H, int N, int d, int dtype, int block_q,
-                    int block_k, const fvattn_route_opts *opts, fvattn_csr *csr, void *ws, size_t ws_bytes,
-                    void *stream) {
-  if (!dtype_ok(dtype)) return FVATTN_ERR_UNSUPPORTED;
-  if (opts == nullptr) return FVATTN_ERR_INVALID;
-  Shape s;
-  int rc = check_shape(B, H, N, d, block_q, block_k, &s);
-  if (rc != FVATTN_OK) return rc;
-  const fvattn_route_opts &o = *opts;
+namespace {
+// Validation of the routing options; FVATTN_OK or the error code.
+int route_opts_check(const fvattn_route_opts &o) {
   if (o.mode == FVATTN_ROUTE_TOPP) {
     if (!(o.p > 0.0 && o.p <= 1.0)) return FVATTN_ERR_INVALID;  // also rejects NaN
     if (o.k_min < 1 || o.k_max < 0 || (o.k_max > 0 && o.k_max < o.k_min)) return FVATTN_ERR_INVALID;
@@ -175,21 +200,78 @@ int fvattn_route_ex(const void *q, const void *k, int B, int H, int N, int d, in
     return FVATTN_ERR_INVALID;
   }
   if (o.window < 0) return FVATTN_ERR_INVALID;
-  if (q == nullptr || k == nullptr || csr == nullptr || ws == nullptr) return FVATTN_ERR_INVALID;
-  if (csr->row_ptr == nullptr || csr->col_idx == nullptr || csr->head_load == nullptr) return FVATTN_ERR_INVALID;
-  if (csr->capacity < (int64_t)s.rows * s.nkb) return FVATTN_ERR_CAPACITY;
-  const RouteWs w = route_ws_layout(s, (char *)ws);
-  if (ws_bytes < w.bytes) return FVATTN_ERR_WORKSPACE;
-  hipStream_t st = (hipStream_t)stream;
+  return FVATTN_OK;
+}
 
+// Pool, select (optionally writing the importance of every block) and, unless `csr_after`
+// is false, the CSR.  Arguments already validated.
+int route_core(const void *q, const void *k, const Shape &s, int N, int d, int dtype, int block_q, int block_k,
+               const fvattn_route_opts &o, fvattn_csr *csr, const RouteWs &w, double *imp, bool csr_after,
+               hipStream_t st) {
+  int rc;
   csr->bh = s.BH; csr->n = N; csr->block_q = block_q; csr->block_k = block_k; csr->nqb = s.nqb; csr->nkb = s.nkb;
   if ((rc = fv::launch_pool_qk(q, k, s.BH, N, d, dtype, block_q, block_k, w.qsw, w.ksw, w.bsum, w.nblk,
                                csr->head_load, s.BH, st)) != FVATTN_OK)
     return rc;
   const double p = o.mode == FVATTN_ROUTE_TOPP ? o.p : 1.0;
   if ((rc = fv::launch_select(w.qsw, w.ksw, s.BH, d, s.nqb, s.nkb, p, w.counts, w.bitmask, s.nkw, csr->head_load,
-                              w.bsum, o.mode, o.topk, o.k_min, o.k_max, o.window, block_q, block_k, N, st)) !=
+                              w.bsum, o.mode, o.topk, o.k_min, o.k_max, o.window, block_q, block_k, N, imp, st)) !=
       FVATTN_OK)
+    return rc;
+  if (!csr_after) return FVATTN_OK;
+  return fv::launch_csr(w.counts, w.bitmask, w.bsum, s.rows, s.nkw, s.nkb, csr->row_ptr, csr->col_idx, st);
+}
+}  // namespace
+
+int fvattn_route_ex(const void *q, const void *k, int B, int H, int N, int d, int dtype, int block_q,
+                    int block_k, const fvattn_route_opts *opts, fvattn_csr *csr, void *ws, size_t ws_bytes,
+                    void *stream) {
+  if (!dtype_ok(dtype)) return FVATTN_ERR_UNSUPPORTED;
+  if (opts == nullptr) return FVATTN_ERR_INVALID;
+  Shape s;
+  int rc = check_shape(B, H, N, d, block_q, block_k, &s);
+  if (rc != FVATTN_OK) return rc;
+  if ((rc = route_opts_check(*opts)) != FVATTN_OK) return rc;
+  if (q == nullptr || k == nullptr || csr == nullptr || ws == nullptr) return FVATTN_ERR_INVALID;
+  if (csr->row_ptr == nullptr || csr->col_idx == nullptr || csr->head_load == nullptr) return FVATTN_ERR_INVALID;
+  if (csr->capacity < (int64_t)s.rows * s.nkb) return FVATTN_ERR_CAPACITY;
+  const RouteWs w = route_ws_layout(s, (char *)ws);
+  if (ws_bytes < w.bytes) return FVATTN_ERR_WORKSPACE;
+  return route_core(q, k, s, N, d, dtype, block_q, block_k, *opts, csr, w, nullptr, true, (hipStream_t)stream);
+}
+
+size_t fvattn_route_sasa_ws_bytes(int B, int H, int N, int d, int block_q, int block_k, int groups) {
+  Shape s;
+  if (check_shape(B, H, N, d, block_q, block_k, &s) != FVATTN_OK) return 0;
+  if (groups < 1 || groups > s.BH || groups > 1024) return 0;
+  return sasa_ws_layout(s, groups, nullptr).bytes;
+}
+
+int fvattn_route_sasa(const void *q, const void *k, int B, int H, int N, int d, int dtype, int block_q,
+                      int block_k, const fvattn_route_opts *ropts, const fvattn_sasa_opts *sopts, fvattn_csr *csr,
+                      void *ws, size_t ws_bytes, void *stream) {
+  if (!dtype_ok(dtype)) return FVATTN_ERR_UNSUPPORTED;
+  if (ropts == nullptr || sopts == nullptr) return FVATTN_ERR_INVALID;
+  Shape s;
+  int rc = check_shape(B, H, N, d, block_q, block_k, &s);
+  if (rc != FVATTN_OK) return rc;
+  if ((rc = route_opts_check(*ropts)) != FVATTN_OK) return rc;
+  const fvattn_sasa_opts &so = *sopts;
+  if (so.groups < 1 || so.groups > s.BH || so.groups > 1024) return FVATTN_ERR_INVALID;
+  if (!(so.alpha >= 0.0 && so.alpha <= 1.0) || !(so.tau >= 0.0 && so.tau <= 1.0)) return FVATTN_ERR_INVALID;
+  if (so.critical < 0) return FVATTN_ERR_INVALID;
+  if (q == nullptr || k == nullptr || csr == nullptr || ws == nullptr) return FVATTN_ERR_INVALID;
+  if (csr->row_ptr == nullptr || csr->col_idx == nullptr || csr->head_load == nullptr) return FVATTN_ERR_INVALID;
+  if (csr->capacity < (int64_t)s.rows * s.nkb) return FVATTN_ERR_CAPACITY;
+  const SasaWs sw = sasa_ws_layout(s, so.groups, (char *)ws);
+  if (ws_bytes < sw.bytes) return FVATTN_ERR_WORKSPACE;
+  const RouteWs w = route_ws_layout(s, (char *)ws);
+  hipStream_t st = (hipStream_t)stream;
+  if ((rc = route_core(q, k, s, N, d, dtype, block_q, block_k, *ropts, csr, w, sw.imp, false, st)) != FVATTN_OK)
+    return rc;
+  if ((rc = fv::launch_sasa(sw.imp, w.bitmask, w.counts, w.bsum, csr->head_load, s.nkw, s.nqb, s.nkb, s.BH,
+                            so.groups, so.critical, so.alpha, so.tau, sw.grp, sw.ghist, sw.tiecnt, sw.tiepre,
+                            so.added, st)) != FVATTN_OK)
     return rc;
   return fv::launch_csr(w.counts, w.bitmask, w.bsum, s.rows, s.nkw, s.nkb, csr->row_ptr, csr->col_idx, st);
 }

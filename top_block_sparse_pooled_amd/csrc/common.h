@@ -48,6 +48,13 @@ __device__ __forceinline__ void unpack16(const u32x4 &c, float *out, float) {
 
 __host__ __device__ constexpr inline int cdiv(int a, int b) { return (a + b - 1) / b; }
 
+// Smallest shift with (width - 1) >> shift < 256: the 8-bit radix digit of a key in a range of
+// `width` keys (radix selects over float64 bit patterns).
+__device__ __forceinline__ int digit_shift(unsigned long long width) {
+  const unsigned long long wm1 = width - 1ull;
+  return wm1 < 256ull ? 0 : 64 - __clzll((long long)wm1) - 8;
+}
+
 // Compute units of the current device (cached per device); 0 on success.
 inline int device_cus(int *cus) {
   static int cache[64] = {0};

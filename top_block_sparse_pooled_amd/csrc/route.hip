@@ -140,13 +140,9 @@ constexpr int kMaxNkw = 40;  // 1280 key blocks
 // count, local window, and the block geometry the window needs.
 struct SelOpts {
   int mode, topk, k_min, k_max, window, bq, bk, N;
+  double *imp;   // optional [rows][nkb]: importance P of every block (SASA candidates); EXT only
 };
 
-// Smallest shift with (width - 1) >> shift < 256: the digit of a key in a range of `width`.
-__device__ __forceinline__ int digit_shift(unsigned long long width) {
-  const unsigned long long wm1 = width - 1ull;
-  return wm1 < 256ull ? 0 : 64 - __clzll((long long)wm1) - 8;
-}
 
 // NWV waves per workgroup (4, or 8 for more than 512 key blocks): wave w holds key tiles
 // w, w + NWV, ... (MAXT of them).  EXT: routing variants (count searches, clamp, window).
@@ -169,6 +165,7 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 ? 2 : 1) void k_select(const dou
   __shared__ int s_state[16];   // 0 searching, 1 unique threshold, 2 ties, 3 keep all, 4 final
   __shared__ int s_bycnt[16];   // search by count instead of mass
   __shared__ unsigned long long s_lo0[16];
+  __shared__ double s_invz[16];     // 1 / Z (importance P = e / Z)
   __shared__ uint32_t s_selcnt[16];
   __shared__ int s_any;
 
@@ -308,6 +305,7 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 ? 2 : 1) void k_select(const dou
     }
     s_target[r] = T;
     s_lo0[r] = lo;
+    if (EXT) s_invz[r] = Z > 0 ? 4503599627370496.0 / (double)Z : 0.0;   // 2^52 / fixed-point Z
     s_lo[r] = lo;
     s_width[r] = (unsigned long long)__double_as_longlong(1.0) + 1ull - lo;
     s_above[r] = 0;
@@ -522,6 +520,24 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 ? 2 : 1) void k_select(const dou
   }
   }   // rounds
 
+  if constexpr (EXT) {
+    // importance of every block of the live rows: the candidates' order for SASA
+    if (sel.imp != nullptr) {
+#pragma unroll
+      for (int k = 0; k < MAXT; ++k) {
+        const int j = 16 * (w + NWV * k) + jl;
+        if (j < nkb) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int r = ig + 4 * v;
+            const int i = 16 * g + r;
+            if (i < nqb) sel.imp[((size_t)bh * nqb + i) * nkb + j] = acc[k][v] * s_invz[r];
+          }
+        }
+      }
+    }
+  }
+
   // ---- write counts, masks, loads (wave w: rows 4w..4w+3)
   for (int rr = 0; rr < RPW; ++rr) {
     const int r = RPW * w + rr;
@@ -661,7 +677,8 @@ template <int D, int MT, int NWV>
 static int launch_select_mt(const double *qsw, const double *ksw, int BH, int nqb, int nkb, double p,
                             int32_t *counts, uint32_t *bitmask, int nkw, int32_t *head_load, int32_t *bsum,
                             const SelOpts &sel, hipStream_t st) {
-  auto kern = (sel.mode != FVATTN_ROUTE_TOPP || sel.k_min > 1 || sel.k_max > 0 || sel.window > 0)
+  auto kern = (sel.mode != FVATTN_ROUTE_TOPP || sel.k_min > 1 || sel.k_max > 0 || sel.window > 0 ||
+               sel.imp != nullptr)
                   ? k_select<D, MT, NWV, true>
                   : k_select<D, MT, NWV, false>;
   int cus = 0, occ = 0;
@@ -697,8 +714,8 @@ static int launch_select_d(const double *qsw, const double *ksw, int BH, int nqb
 
 int launch_select(const double *qsw, const double *ksw, int BH, int d, int nqb, int nkb, double p,
                   int32_t *counts, uint32_t *bitmask, int nkw, int32_t *head_load, int32_t *bsum, int mode, int topk,
-                  int k_min, int k_max, int window, int bq, int bk, int N, hipStream_t st) {
-  const SelOpts sel{mode, topk, k_min, k_max, window, bq, bk, N};
+                  int k_min, int k_max, int window, int bq, int bk, int N, double *imp, hipStream_t st) {
+  const SelOpts sel{mode, topk, k_min, k_max, window, bq, bk, N, imp};
   if (d == 128) return launch_select_d<128>(qsw, ksw, BH, nqb, nkb, p, counts, bitmask, nkw, head_load, bsum, sel, st);
   return launch_select_d<64>(qsw, ksw, BH, nqb, nkb, p, counts, bitmask, nkw, head_load, bsum, sel, st);
 }

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfvattn.so")
-SOURCES = ["abi.hip", "route.hip", "attn.hip"]
+SOURCES = ["abi.hip", "route.hip", "attn.hip", "sasa.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
