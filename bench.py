@@ -123,6 +123,9 @@ def main():
     ap.add_argument("--k-min", type=int, default=1, help="lower clamp of the Top-p count")
     ap.add_argument("--k-max", type=int, default=0, help="upper clamp of the Top-p count (0: none)")
     ap.add_argument("--window", type=int, default=0, help="local window of key blocks kept around each query block")
+    ap.add_argument("--sasa-groups", type=int, default=0, help="SASA over this many head groups (0: off)")
+    ap.add_argument("--sasa-alpha", type=float, default=0.5, help="SASA augmentation coefficient")
+    ap.add_argument("--sasa-tau", type=float, default=0.0, help="SASA trigger threshold")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -154,13 +157,21 @@ def main():
     o = torch.empty(qd.shape, dtype=out_dtype or tdt, device=dev)
 
     variant = dict(mode=args.mode, topk=args.topk, k_min=args.k_min, k_max=args.k_max, window=args.window)
+    sws = None
+    if args.sasa_groups > 0:
+        sws = torch.empty(fv.lib().fvattn_route_sasa_ws_bytes(1, w.H, w.N, w.d, w.block_q, w.block_k,
+                                                               args.sasa_groups), dtype=torch.uint8, device=dev)
     if args.mode == "topk" and args.topk < 1:
         raise SystemExit("--mode topk needs --topk >= 1")
 
     def step(ev=None):
         if ev is not None:
             ev[0].record()
-        fv.route(qd, kd, w.block_q, w.block_k, p, csr=csr, ws=rws, **variant)
+        if args.sasa_groups > 0:
+            fv.route_sasa(qd, kd, w.block_q, w.block_k, p, groups=args.sasa_groups, alpha=args.sasa_alpha,
+                          tau=args.sasa_tau, csr=csr, ws=sws, **variant)
+        else:
+            fv.route(qd, kd, w.block_q, w.block_k, p, csr=csr, ws=rws, **variant)
         if ev is not None:
             ev[1].record()
         fv.attn_plan(vd, csr, aws, args.schedule)
@@ -199,6 +210,20 @@ def main():
     log(f"[bench] ms/step {ms_step:.3f} (route {route_ms:.3f}, plan {plan_ms:.3f}, attn {attn_ms:.3f}); "
         f"attn {attn_tflops:.1f} TFLOP/s; route {route_gbps:.0f} GB/s; kept {nnz / (w.rows * w.nkb):.4f}")
 
+    sasa_info = None
+    if args.sasa_groups > 0:
+        R = args.sasa_groups
+        after = csr.head_load.cpu().numpy().astype(np.int64)
+        base = fv.route(qd, kd, w.block_q, w.block_k, p, **variant).head_load.cpu().numpy().astype(np.int64)
+        grp = np.arange(w.H) * R // w.H
+        Lb = np.bincount(grp, weights=base, minlength=R)
+        La = np.bincount(grp, weights=after, minlength=R)
+        sasa_info = dict(groups=R, alpha=args.sasa_alpha, tau=args.sasa_tau, added=int(after.sum() - base.sum()),
+                         group_load_before=[int(x) for x in Lb], group_load_after=[int(x) for x in La],
+                         max_over_mean_before=float(Lb.max() / Lb.mean()),
+                         max_over_mean_after=float(La.max() / La.mean()))
+        log(f"[bench] sasa {json.dumps(sasa_info)}")
+
     traffic = None
     prof = os.path.join(ROOT, "profiles", f"attn_counters_{w.name}.json")
     if os.path.exists(prof):
@@ -206,7 +231,8 @@ def main():
             pc = json.load(open(prof))
             same = (pc.get("kernel_source_sha") == _attn_source_sha() and pc.get("p") == p
                     and pc.get("schedule") == args.schedule and pc.get("routing", "topp") == "topp"
-                    and args.mode == "topp" and args.k_min == 1 and args.k_max == 0 and args.window == 0)
+                    and args.mode == "topp" and args.k_min == 1 and args.k_max == 0 and args.window == 0
+                    and args.sasa_groups == 0)
             if same:
                 traffic = pc.get("bytes_per_launch")
         except Exception:
@@ -261,6 +287,7 @@ def main():
         config=dict(workload=w.name, B=1, H=w.H, N=w.N, d=w.d, block_q=w.block_q, block_k=w.block_k, p=p,
                     routing=(variant if (args.mode != "topp" or args.k_min != 1 or args.k_max or args.window)
                              else "topp"),
+                    sasa=sasa_info,
                     schedule=args.schedule, out=args.out, nnz=nnz, kept_frac=nnz / (w.rows * w.nkb),
                     executed_tflop=flops / 1e12, nominal_tflop=flops_nominal / 1e12),
         stages_ms=dict(route=route_ms, plan=plan_ms, attn=attn_ms),
