@@ -817,6 +817,10 @@ __global__ __launch_bounds__(512, 1) void k_attn_pp(
     };
 
     int ep = -1, ec = entry(0), e1 = entry(1);   // entries of steps i-1, i, i+1
+    // X_i needs the entry of step i+2: it is read from LDS one phase ahead, so the read's
+    // latency is spent in the M phase in between
+    auto entry_lds = [&](int i) -> int { const int e = 2 * i + grp; return e < n ? s_list[e] : -1; };
+    int enx = entry_lds(2);
     // prologue in the order a previous X phase would use: K_0, then K_1 and V_0
     load_k(ec >> 4, K0[grp]);      // (entry -1 >> 4 = -1: an empty load)
     load_k(e1 >> 4, K1[grp]);
@@ -897,7 +901,8 @@ __global__ __launch_bounds__(512, 1) void k_attn_pp(
     auto phaseX = [&](int i, uint8_t *kdst, uint8_t *vdst) {
       lds_barrier();
       // ---- X_i
-      const int e2 = entry(i + 2);
+      const int e2 = __builtin_amdgcn_readfirstlane(enx);
+      enx = entry_lds(i + 3);
       load_k(e2 >> 4, kdst);
       load_v(e1 >> 4, vdst);
       if (dos) {
@@ -971,6 +976,9 @@ __global__ __launch_bounds__(512, 1) void k_attn_pp(
       phaseX(i + 1, K1[grp], V0[grp]);
       phaseM(K0[grp], V1[grp]);                    // M_{i+2}
     }
+    // The last X phase's tile loads (empty: zeros from past the buffer end) may still be in
+    // flight into the buffers the merge reuses as its exchange area.
+    wait_vmcnt<0>();
     if (grp == 0) lds_barrier();   // equal barrier counts for both groups
     lds_barrier();                 // both groups are past their last phase: tile buffers free
 

@@ -129,9 +129,16 @@ __global__ __launch_bounds__(256) void k_pool(PoolArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------
-// k_select: scores, softmax, Top-p cut for 16 query blocks of one head per item.
-// Persistent: grid = min(resident workgroups, items), at least 8; 256 threads.
-// MAXT = key tiles (of 16) per wave.
+// k_select: scores, softmax and the Top-p cut (or a routing variant) for 16 query blocks of
+// one head per item.  Persistent: grid = min(resident workgroups, items), at least 8.
+// NWV waves (4, or 8 for more than 512 key blocks); MAXT key tiles of 16 per wave.
+//   1. Scores for the 16 rows on the float64 MFMA, wave w holding key tiles w, w + NWV, ...;
+//      row maxima, e = exp(s - max), fixed-point row sums Z and row minima of e across the
+//      waves (two workgroup barriers).
+//   2. The e values go to LDS as whole rows (RB rows at a time), and each wave then resolves
+//      its rows alone: the row's values sit in registers (lane l: key blocks l + 64 t), the
+//      radix passes use a histogram private to the wave, and the kept set leaves as 64-bit
+//      ballots.  No workgroup barrier inside the selection.
 // Outputs counts[row] and the kept-bit mask bitmask[row][nkw]; adds loads to head_load.
 // ---------------------------------------------------------------------------------------
 constexpr int kMaxNkw = 40;  // 1280 key blocks
@@ -143,9 +150,123 @@ struct SelOpts {
   double *imp;   // optional [rows][nkb]: importance P of every block (SASA candidates); EXT only
 };
 
+constexpr double kFix52 = 4503599627370496.0;  // 2^52: masses as fixed point
 
-// NWV waves per workgroup (4, or 8 for more than 512 key blocks): wave w holds key tiles
-// w, w + NWV, ... (MAXT of them).  EXT: routing variants (count searches, clamp, window).
+// Kept set of one row by the wave: the shortest prefix of the (e descending, index ascending)
+// order whose mass (bycnt = false: fixed-point e, target T) or count (bycnt = true, target T)
+// reaches T.  ev[t] is e of key block lane + 64 t; valid below nkb.  Search range of keys (the
+// float64 bit patterns of e, monotone for e >= 0): [lo0, bits(1.0)].  Each radix pass splits
+// the range into 256 digit bins, walks the histogram from the largest digit down to the bin
+// where the cumulative mass from the top reaches T, and narrows the range to that bin, until
+// the bin holds one key or one key value (ties, resolved toward lower indices).  Returns the
+// kept-bit word of key blocks 32 lane .. 32 lane + 31 (zero for lanes past the row) and sets
+// `count` to the number of kept blocks.
+template <int NPL>
+__device__ __forceinline__ uint32_t select_row(const double (&ev)[NPL], int nkb, bool bycnt, unsigned long long T,
+                                               unsigned long long lo0, bool keep_all,
+                                               unsigned long long *__restrict__ hm, uint32_t *__restrict__ hc,
+                                               int &count) {
+  const int lane = threadIdx.x & 63;
+  unsigned long long lo = lo0;
+  unsigned long long width = (unsigned long long)__double_as_longlong(1.0) + 1ull - lo0;
+  unsigned long long above = 0;
+  int st = keep_all ? 3 : 0;   // 0 searching, 1 unique threshold key, 2 tied threshold keys, 3 all
+  uint32_t ntie = 0;
+  for (int pass = 0; pass < 8 && st == 0; ++pass) {
+    const int sh = digit_shift(width);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      hm[4 * lane + q] = 0ull;
+      hc[4 * lane + q] = 0u;
+    }
+    // (LDS operations of one wave take effect in issue order; the fences only keep the
+    // compiler from moving them)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+#pragma unroll
+    for (int t = 0; t < NPL; ++t) {
+      const unsigned long long off = (unsigned long long)__double_as_longlong(ev[t]) - lo;
+      if (lane + 64 * t < nkb && off < width) {
+        const int dg = (int)(off >> sh);
+        atomicAdd(&hc[dg], 1u);
+        if (!bycnt) atomicAdd(&hm[dg], (unsigned long long)(ev[t] * kFix52));
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    unsigned long long m4[4];
+    uint32_t c4[4];
+    unsigned long long ms = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      c4[q] = hc[4 * lane + q];
+      m4[q] = bycnt ? (unsigned long long)c4[q] : hm[4 * lane + q];
+      ms += m4[q];
+    }
+    // mass of the digits held by higher lanes (larger keys)
+    unsigned long long sm = ms;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const unsigned long long o = __shfl_down(sm, off);
+      if (lane + off < 64) sm += o;
+    }
+    unsigned long long acc = above + (sm - ms);
+    int dig = -1;
+    unsigned long long nab = 0;
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int q = 3; q >= 0; --q) {
+      if (m4[q] > 0 && acc < T && T <= acc + m4[q]) {
+        dig = 4 * lane + q;
+        nab = acc;
+        cnt = c4[q];
+      }
+      acc += m4[q];
+    }
+    const unsigned long long bal = __ballot(dig >= 0);
+    if (bal == 0ull) {   // unreachable: the range always holds the crossing
+      st = 3;
+      break;
+    }
+    const int L = __ffsll((long long)bal) - 1;
+    dig = __shfl(dig, L);
+    above = __shfl(nab, L);
+    cnt = __shfl(cnt, L);
+    lo += (unsigned long long)dig << sh;
+    width = 1ull << sh;
+    ntie = cnt;
+    if (cnt == 1) st = 1;
+    else if (sh == 0) st = 2;
+  }
+  const unsigned long long hi = lo + width;
+  uint32_t need = 0;
+  if (st == 2) {
+    const unsigned long long rem = T - above;
+    const unsigned long long mt = (unsigned long long)(__longlong_as_double((long long)lo) * kFix52);
+    if (bycnt) need = (uint32_t)min((unsigned long long)ntie, rem);
+    else need = mt == 0 ? ntie : (uint32_t)min((unsigned long long)ntie, (rem + mt - 1) / mt);
+  }
+  uint32_t cum = 0;   // ties taken so far (ascending key block)
+  uint32_t word = 0;
+  count = 0;
+#pragma unroll
+  for (int t = 0; t < NPL; ++t) {
+    const bool valid = lane + 64 * t < nkb;
+    const unsigned long long key = (unsigned long long)__double_as_longlong(ev[t]);
+    bool keep = valid && (st == 3 || key >= hi || (st == 1 && key >= lo));
+    if (st == 2) {
+      const bool tie = valid && key == lo;
+      const unsigned long long bt = __ballot(tie);
+      const uint32_t rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(bt >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bt, 0u));
+      keep = keep || (tie && cum + rank < need);
+      cum += (uint32_t)__popcll(bt);
+    }
+    const unsigned long long mt = __ballot(keep);
+    if (lane == 2 * t) word = (uint32_t)mt;
+    if (lane == 2 * t + 1) word = (uint32_t)(mt >> 32);
+    count += (int)__popcll(mt);
+  }
+  return word;
+}
+
 template <int D, int MAXT, int NWV, bool EXT>
 __global__ __launch_bounds__(64 * NWV, NWV == 4 ? 2 : 1) void k_select(const double *__restrict__ qsw,
                                                 const double *__restrict__ ksw, int nqb, int nkb,
@@ -153,25 +274,22 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 ? 2 : 1) void k_select(const dou
                                                 uint32_t *__restrict__ bitmask, int nkw,
                                                 int32_t *__restrict__ head_load, int32_t *__restrict__ bsum,
                                                 int BH, SelOpts sel) {
-  constexpr int KS = D / 4;  // MFMA k-steps
-  __shared__ uint32_t h_cnt[16][256];
-  __shared__ unsigned long long h_mass[16][256];
-  __shared__ uint32_t s_kept[16][kMaxNkw];
-  __shared__ uint32_t s_ties[16][kMaxNkw];
+  constexpr int KS = D / 4;               // MFMA k-steps
+  constexpr int KCAP = 16 * NWV * MAXT;   // key blocks the tiles cover
+  constexpr int NPL = KCAP / 64;          // values per lane in the row phase
+  constexpr int RB = NWV == 4 ? 16 : 8;   // rows staged in LDS at once
+  constexpr int NB = 16 / RB;
+  constexpr int RPW = RB / NWV;           // rows per wave per batch
+  static_assert(KCAP % 64 == 0 && RB % NWV == 0 && (RB / 4) * 4 == RB, "row phase geometry");
+  __shared__ double s_e[RB][KCAP];
+  __shared__ unsigned long long h_mass[NWV][256];
+  __shared__ uint32_t h_cnt[NWV][256];
   __shared__ double s_part[NWV][16];
   __shared__ unsigned long long s_zpart[NWV][16];
-  __shared__ unsigned long long s_lo[16], s_width[16], s_above[16], s_target[16];
   __shared__ double s_minpart[NWV][16];
-  __shared__ int s_state[16];   // 0 searching, 1 unique threshold, 2 ties, 3 keep all, 4 final
-  __shared__ int s_bycnt[16];   // search by count instead of mass
-  __shared__ unsigned long long s_lo0[16];
-  __shared__ double s_invz[16];     // 1 / Z (importance P = e / Z)
-  __shared__ uint32_t s_selcnt[16];
-  __shared__ int s_any;
 
-  constexpr int NT = 64 * NWV;      // threads
-  constexpr int RPW = 16 / NWV;     // rows resolved per wave
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nqg = (nqb + 15) >> 4;
   const int nkt = (nkb + 15) >> 4;
 
@@ -191,30 +309,35 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 ? 2 : 1) void k_select(const dou
   for (int k = 0; k < MAXT; ++k) acc[k] = d4{0.0, 0.0, 0.0, 0.0};
   {
     const double *qa = qsw + ((size_t)(bh * nqg + g) * KS) * 64 + lane;
-    // k-step outer, tiles inner: MAXT independent accumulators, and the operands of step s+1
-    // (one of qbar, MAXT of kbar) are in flight while step s runs.  Tiles past the last read a
-    // valid tile (their key columns are >= nkb and ignored below), so the loop has no branches.
+    // k-step outer, tiles inner: MAXT independent accumulators.  The operands of PF k-steps
+    // (one of qbar, MAXT of kbar each) are in flight ahead of the MFMAs that use them, which
+    // covers the L2 latency of the pooled keys.  Tiles past the last read a valid tile (their
+    // key columns are >= nkb and ignored below), so the loop has no branches.
+    constexpr int PF = MAXT >= 10 ? 1 : (MAXT >= 8 ? 2 : 3);
     const double *kb[MAXT];
 #pragma unroll
     for (int k = 0; k < MAXT; ++k) kb[k] = ksw + ((size_t)(bh * nkt + min(w + NWV * k, nkt - 1)) * KS) * 64 + lane;
-    double acur = qa[0], bcur[MAXT];
+    double abuf[PF], bbuf[PF][MAXT];
 #pragma unroll
-    for (int k = 0; k < MAXT; ++k) bcur[k] = kb[k][0];
+    for (int s = 0; s < PF; ++s) {
+      abuf[s] = qa[s * 64];
+#pragma unroll
+      for (int k = 0; k < MAXT; ++k) bbuf[s][k] = kb[k][s * 64];
+    }
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      double anxt = 0.0, bnxt[MAXT];
-      if (s + 1 < KS) {
-        anxt = qa[(s + 1) * 64];
+      const int slot = s % PF;
+      const double a = abuf[slot];
+      double b[MAXT];
 #pragma unroll
-        for (int k = 0; k < MAXT; ++k) bnxt[k] = kb[k][(s + 1) * 64];
+      for (int k = 0; k < MAXT; ++k) b[k] = bbuf[slot][k];
+      if (s + PF < KS) {
+        abuf[slot] = qa[(s + PF) * 64];
+#pragma unroll
+        for (int k = 0; k < MAXT; ++k) bbuf[slot][k] = kb[k][(s + PF) * 64];
       }
 #pragma unroll
-      for (int k = 0; k < MAXT; ++k) acc[k] = __builtin_amdgcn_mfma_f64_16x16x4f64(acur, bcur[k], acc[k], 0, 0, 0);
-      if (s + 1 < KS) {
-        acur = anxt;
-#pragma unroll
-        for (int k = 0; k < MAXT; ++k) bcur[k] = bnxt[k];
-      }
+      for (int k = 0; k < MAXT; ++k) acc[k] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b[k], acc[k], 0, 0, 0);
     }
   }
 
@@ -248,8 +371,7 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 ? 2 : 1) void k_select(const dou
     mx[v] = m;
   }
 
-  // ---- e = exp(s - max) (in place), fixed-point masses, Z
-  constexpr double kFix = 4503599627370496.0;  // 2^52
+  // ---- e = exp(s - max) (in place; 0 past nkb), fixed-point masses, Z, minimum of e
   unsigned long long zs[4] = {0, 0, 0, 0};
   double mn[4] = {1.0, 1.0, 1.0, 1.0};
 #pragma unroll
@@ -259,7 +381,7 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 ? 2 : 1) void k_select(const dou
     for (int v = 0; v < 4; ++v) {
       const double e = (j < nkb) ? exp(acc[k][v] - mx[v]) : 0.0;
       acc[k][v] = e;
-      zs[v] += (unsigned long long)(e * kFix);
+      zs[v] += (unsigned long long)(e * kFix52);
       if (j < nkb) mn[v] = fmin(mn[v], e);
     }
   }
@@ -275,305 +397,99 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 ? 2 : 1) void k_select(const dou
       s_minpart[w][ig + 4 * v] = mn[v];
     }
   }
-  __syncthreads();
-  // ---- per-row selection setup.  A row searches by mass (Top-p: the shortest prefix of the
-  // descending order whose mass reaches p Z) or by count (top-k, or a clamped Top-p count):
-  // the same radix walk over mass or count histograms.
-  if (tid < 16) {
-    const int r = tid;
-    unsigned long long Z = 0;
-    double emin = 1.0;
-    for (int ww = 0; ww < NWV; ++ww) {
-      Z += s_zpart[ww][r];
-      emin = fmin(emin, s_minpart[ww][r]);
-    }
-    // search range of keys (float64 bit patterns of e, monotone for e >= 0): [e_min, 1.0]
-    const unsigned long long lo = (unsigned long long)__double_as_longlong(emin);
-    const bool live = (16 * g + r) < nqb;
-    unsigned long long T;
-    int st;
-    if (EXT && sel.mode == FVATTN_ROUTE_TOPK) {
-      T = (unsigned long long)sel.topk;
-      st = (!live || sel.topk >= nkb) ? 3 : 0;
-      s_bycnt[r] = 1;
-    } else {
-      T = (unsigned long long)ceil(p * (double)Z);
-      if (T > Z) T = Z;
-      if (T < 1) T = 1;
-      st = (!live || p >= 1.0) ? 3 : 0;
-      s_bycnt[r] = 0;
-    }
-    s_target[r] = T;
-    s_lo0[r] = lo;
-    if (EXT) s_invz[r] = Z > 0 ? 4503599627370496.0 / (double)Z : 0.0;   // 2^52 / fixed-point Z
-    s_lo[r] = lo;
-    s_width[r] = (unsigned long long)__double_as_longlong(1.0) + 1ull - lo;
-    s_above[r] = 0;
-    s_selcnt[r] = 0;
-    s_state[r] = st;
-  }
-  __syncthreads();
 
-  // Round 0 selects; with a clamp on the Top-p count, round 1 re-selects by count the rows
-  // whose kept count lies outside [k_min, k_max] (other rows are final: state 4).
-  const bool clamp = EXT && sel.mode != FVATTN_ROUTE_TOPK && (sel.k_min > 1 || sel.k_max > 0);
-  for (int round = 0; round < (EXT ? 2 : 1); ++round) {
-    // ---- radix select over the key range [lo, lo + width): each pass splits the range into
-    // 256 equal digit bins (log-linear in e), finds the bin where the cumulative mass (or
-    // count) from the top crosses the target, and narrows the range to that bin.  The first
-    // range spans the row's own [e_min, 1], so elements spread over the bins.
-  for (int pass = 0; pass < 8; ++pass) {
-    if (tid == 0) {
-      int any = 0;
-      for (int r = 0; r < 16; ++r) any |= (s_state[r] == 0);
-      s_any = any;
-    }
-    for (int i = tid; i < 16 * 256; i += NT) {
-      (&h_cnt[0][0])[i] = 0;
-      (&h_mass[0][0])[i] = 0;
-    }
-    __syncthreads();
-    if (!s_any) break;
-    unsigned long long rlo[4], rw[4];
-    int rsh[4];
-    bool act[4];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int r = ig + 4 * v;
-      rlo[v] = s_lo[r];
-      rw[v] = s_width[r];
-      rsh[v] = digit_shift(rw[v]);
-      act[v] = s_state[r] == 0;
-    }
+  for (int b = 0; b < NB; ++b) {
+    // ---- stage rows [b RB, b RB + RB): lane (ig, jl) holds rows ig + 4v of its key columns
 #pragma unroll
     for (int k = 0; k < MAXT; ++k) {
       const int j = 16 * (w + NWV * k) + jl;
-      if (j < nkb) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const unsigned long long off = (unsigned long long)__double_as_longlong(acc[k][v]) - rlo[v];
-          if (act[v] && off < rw[v]) {
-            const int dg = (int)(off >> rsh[v]);
-            const int r = ig + 4 * v;
-            atomicAdd(&h_cnt[r][dg], 1u);
-            atomicAdd(&h_mass[r][dg], (unsigned long long)(acc[k][v] * kFix));
-          }
-        }
-      }
+      for (int v = b * RB / 4; v < (b + 1) * RB / 4; ++v) s_e[ig + 4 * v - b * RB][j] = acc[k][v];
     }
     __syncthreads();
-    // wave w resolves rows 4w .. 4w+3: find the digit where the mass crosses the target
+    // ---- selection: wave w resolves rows b RB + rr NWV + w
     for (int rr = 0; rr < RPW; ++rr) {
-      const int r = RPW * w + rr;
-      if (s_state[r] != 0) continue;  // uniform across the wave
-      // the walk runs over masses (Top-p) or counts (top-k, clamped count)
-      const bool bc = EXT && s_bycnt[r] != 0;
-      unsigned long long m4[4];
-      uint32_t c4[4];
-      unsigned long long ms = 0;
+      const int r = b * RB + rr * NWV + w;
+      const int i = 16 * g + r;
+      if (i >= nqb) continue;   // wave-uniform
+      const size_t row = (size_t)bh * nqb + i;
+      double ev[NPL];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        c4[q] = h_cnt[r][4 * lane + q];
-        m4[q] = bc ? (unsigned long long)c4[q] : h_mass[r][4 * lane + q];
-        ms += m4[q];
+      for (int t = 0; t < NPL; ++t) ev[t] = s_e[r - b * RB][lane + 64 * t];
+      unsigned long long Z = 0;
+      double emin = 1.0;
+#pragma unroll
+      for (int ww = 0; ww < NWV; ++ww) {
+        Z += s_zpart[ww][r];
+        emin = fmin(emin, s_minpart[ww][r]);
       }
-      // exclusive suffix sums over lanes (higher lanes hold larger digits)
-      unsigned long long sm = ms;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const unsigned long long om = __shfl_down(sm, off);
-        if (lane + off < 64) sm += om;
-      }
-      unsigned long long above_m = sm - ms;  // mass of digits held by higher lanes
-      const unsigned long long base = s_above[r];
-      const unsigned long long T = s_target[r];
-      const unsigned long long lo0 = s_lo[r], w0 = s_width[r];
-      const int sh = digit_shift(w0);
-      for (int q = 3; q >= 0; --q) {
-        const unsigned long long lo = base + above_m;
-        if (m4[q] > 0 && lo < T && T <= lo + m4[q]) {
-          s_above[r] = lo;
-          s_lo[r] = lo0 + ((unsigned long long)(4 * lane + q) << sh);
-          s_width[r] = 1ull << sh;
-          s_selcnt[r] = c4[q];
-          if (c4[q] == 1) s_state[r] = 1;         // the threshold block is unique
-          else if (sh == 0) s_state[r] = 2;       // several blocks share the threshold key
-        }
-        above_m += m4[q];
-      }
-    }
-    __syncthreads();
-  }
-
-  // ---- mark kept blocks
-  for (int i = tid; i < 16 * kMaxNkw; i += NT) {
-    if (s_state[i / kMaxNkw] == 4) continue;   // final from the previous round
-    (&s_kept[0][0])[i] = 0;
-    (&s_ties[0][0])[i] = 0;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int k = 0; k < MAXT; ++k) {
-    const int j = 16 * (w + NWV * k) + jl;
-    if (j < nkb) {
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int r = ig + 4 * v;
-        const int st = s_state[r];
-        if (st == 4) continue;
-        const unsigned long long key = (unsigned long long)__double_as_longlong(acc[k][v]);
-        const unsigned long long lo = s_lo[r], hi = lo + s_width[r];
-        const uint32_t bit = 1u << (j & 31);
-        const bool in_range = key >= lo && key < hi;
-        if (st == 3 || key >= hi || (in_range && st == 1))
-          atomicOr(&s_kept[r][j >> 5], bit);
-        else if (in_range && st == 2)
-          atomicOr(&s_ties[r][j >> 5], bit);
-      }
-    }
-  }
-  __syncthreads();
-  // ties (identical importance): the lowest indices first, as many as the mass requires.
-  // Every tied element has the same fixed-point mass; any holder publishes it.
-  __shared__ unsigned long long s_mt[16];
-#pragma unroll
-  for (int k = 0; k < MAXT; ++k) {
-    const int j = 16 * (w + NWV * k) + jl;
-    if (j < nkb) {
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int r = ig + 4 * v;
-        if (s_state[r] == 2 && (s_ties[r][j >> 5] >> (j & 31) & 1u))
-          s_mt[r] = (unsigned long long)(acc[k][v] * kFix);  // identical for all ties
-      }
-    }
-  }
-  __syncthreads();
-  for (int rr = 0; rr < RPW; ++rr) {
-    const int r = RPW * w + rr;
-    if (s_state[r] != 2) continue;
-    const unsigned long long rem = s_target[r] - s_above[r];
-    const unsigned long long mt = s_mt[r];
-    const uint32_t ntie = s_selcnt[r];
-    uint32_t need;
-    if (EXT && s_bycnt[r])
-      need = (uint32_t)min((unsigned long long)ntie, rem);   // count search: rem blocks
-    else
-      need = (mt == 0) ? ntie : (uint32_t)min((unsigned long long)ntie, (rem + mt - 1) / mt);
-    uint32_t word = lane < nkw ? s_ties[r][lane] : 0u;
-    const uint32_t pc = __popc(word);
-    uint32_t incl = pc;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint32_t o = __shfl_up(incl, off);
-      if (lane >= off) incl += o;
-    }
-    const uint32_t excl = incl - pc;
-    if (lane < nkw && excl < need) {
-      uint32_t take = need - excl;
-      uint32_t keep = 0, wd = word;
-      while (wd && take) {
-        const uint32_t b = wd & (0u - wd);
-        keep |= b;
-        wd ^= b;
-        --take;
-      }
-      s_kept[r][lane] |= keep;
-    }
-  }
-  __syncthreads();
-
-
-  if constexpr (EXT) {
-  if (!clamp || round == 1) break;
-  for (int rr = 0; rr < RPW; ++rr) {
-    const int r = RPW * w + rr;
-    uint32_t word = lane < nkw ? s_kept[r][lane] : 0u;
-    int c = __popc(word);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) c += __shfl_xor(c, off);
-    if (lane == 0) {
-      int tgt = max(c, sel.k_min);
-      if (sel.k_max > 0) tgt = min(tgt, sel.k_max);
-      tgt = min(tgt, nkb);
-      if ((16 * g + r) < nqb && tgt != c) {
-        s_bycnt[r] = 1;
-        s_target[r] = (unsigned long long)tgt;
-        s_lo[r] = s_lo0[r];
-        s_width[r] = (unsigned long long)__double_as_longlong(1.0) + 1ull - s_lo0[r];
-        s_above[r] = 0;
-        s_selcnt[r] = 0;
-        s_state[r] = tgt >= nkb ? 3 : 0;
+      const unsigned long long lo0 = (unsigned long long)__double_as_longlong(emin);
+      // search by mass (Top-p) or by count (top-k, or a clamped Top-p count)
+      bool bycnt = false;
+      unsigned long long T;
+      bool all;
+      if (EXT && sel.mode == FVATTN_ROUTE_TOPK) {
+        bycnt = true;
+        T = (unsigned long long)sel.topk;
+        all = sel.topk >= nkb;
       } else {
-        s_state[r] = 4;
+        T = (unsigned long long)ceil(p * (double)Z);
+        if (T > Z) T = Z;
+        if (T < 1) T = 1;
+        all = p >= 1.0;
       }
-    }
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int any = 0;
-    for (int r = 0; r < 16; ++r) any |= (s_state[r] != 4);
-    s_any = any;
-  }
-  __syncthreads();
-  if (!s_any) break;
-  }
-  }   // rounds
-
-  if constexpr (EXT) {
-    // importance of every block of the live rows: the candidates' order for SASA
-    if (sel.imp != nullptr) {
-#pragma unroll
-      for (int k = 0; k < MAXT; ++k) {
-        const int j = 16 * (w + NWV * k) + jl;
-        if (j < nkb) {
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int r = ig + 4 * v;
-            const int i = 16 * g + r;
-            if (i < nqb) sel.imp[((size_t)bh * nqb + i) * nkb + j] = acc[k][v] * s_invz[r];
-          }
+      int c;
+      // lane L < nkw holds kept word L (key blocks 32 L .. 32 L + 31)
+      uint32_t word = select_row<NPL>(ev, nkb, bycnt, T, lo0, all, h_mass[w], h_cnt[w], c);
+      if (EXT && !bycnt && (sel.k_min > 1 || sel.k_max > 0)) {
+        // clamp of the Top-p count: re-select by count when it lies outside [k_min, k_max]
+        int tgt = max(c, sel.k_min);
+        if (sel.k_max > 0) tgt = min(tgt, sel.k_max);
+        tgt = min(tgt, nkb);
+        if (tgt != c) word = select_row<NPL>(ev, nkb, true, (unsigned long long)tgt, lo0, tgt >= nkb, h_mass[w], h_cnt[w], c);
+      }
+      if (EXT && sel.window > 0 && lane < nkw) {
+        // local window: key blocks within `window` of those overlapping the query block's tokens
+        const int t0 = i * sel.bq, t1 = min(t0 + sel.bq, sel.N) - 1;
+        const int ja = max(0, t0 / sel.bk - sel.window), jb = min(nkb - 1, t1 / sel.bk + sel.window);
+        const int lo_j = max(ja, 32 * lane), hi_j = min(jb, 32 * lane + 31);
+        if (lo_j <= hi_j) {
+          const int nbits = hi_j - lo_j + 1;
+          word |= (nbits == 32 ? 0xffffffffu : ((1u << nbits) - 1u)) << (lo_j - 32 * lane);
         }
       }
-    }
-  }
-
-  // ---- write counts, masks, loads (wave w: rows 4w..4w+3)
-  for (int rr = 0; rr < RPW; ++rr) {
-    const int r = RPW * w + rr;
-    const int i = 16 * g + r;
-    if (i >= nqb) continue;
-    const size_t row = (size_t)bh * nqb + i;
-    uint32_t word = lane < nkw ? s_kept[r][lane] : 0u;
-    if (EXT && sel.window > 0 && lane < nkw) {
-      // local window: key blocks within `window` of those overlapping the query block's tokens
-      const int t0 = i * sel.bq, t1 = min(t0 + sel.bq, sel.N) - 1;
-      const int ja = max(0, t0 / sel.bk - sel.window), jb = min(nkb - 1, t1 / sel.bk + sel.window);
-      const int lo_j = max(ja, 32 * lane), hi_j = min(jb, 32 * lane + 31);
-      if (lo_j <= hi_j) {
-        const int nbits = hi_j - lo_j + 1;
-        word |= (nbits == 32 ? 0xffffffffu : ((1u << nbits) - 1u)) << (lo_j - 32 * lane);
+      if (EXT && sel.window > 0) {
+        c = __popc(word);
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) c += __shfl_xor(c, off);
+      }
+      if (lane < nkw) bitmask[row * nkw + lane] = word;
+      if (lane == 0) {
+        counts[row] = c;
+        atomicAdd(&head_load[bh], c);
+        atomicAdd(&bsum[row >> 6], c);   // per-64-row sums for the CSR scan
+      }
+      if (EXT && sel.imp != nullptr) {
+        // importance of every block: the candidates' order for SASA
+        const double invz = Z > 0 ? kFix52 / (double)Z : 0.0;   // 1 / Z with Z in 2^-52 units
+#pragma unroll
+        for (int t = 0; t < NPL; ++t)
+          if (lane + 64 * t < nkb) sel.imp[row * nkb + lane + 64 * t] = ev[t] * invz;
       }
     }
-    if (lane < nkw) bitmask[row * nkw + lane] = word;
-    int c = __popc(word);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) c += __shfl_xor(c, off);
-    if (lane == 0) {
-      counts[row] = c;
-      atomicAdd(&head_load[bh], c);
-      atomicAdd(&bsum[row >> 6], c);   // per-64-row sums for the CSR scan
-    }
+    __syncthreads();   // staged rows and partial sums consumed before they are overwritten
   }
-  __syncthreads();   // LDS of this item fully consumed before the next item writes it
   }
 }
 
 // ---------------------------------------------------------------------------------------
 // k_csr: row_ptr (exclusive scan of counts) and ascending col_idx from the kept masks.
 // grid = cdiv(rows, 64), 256 threads: workgroup b owns rows [64b, 64b + 64); its offset is
-// the sum of the per-64-row sums before it.  Each wave expands 16 rows, 64 key blocks per
-// step: a ballot of the kept bits gives every kept block its output slot (coalesced writes).
+// the sum of the per-64-row sums before it.  Each wave expands 16 rows: lane L holds word L
+// of a row's mask (all 16 rows' words are loaded up front), and each 64-block chunk of the
+// row is one 64-bit mask from two lanes, whose set bits give every kept block its output slot
+// (coalesced writes).
 // ---------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_csr(const int32_t *__restrict__ counts,
                                              const uint32_t *__restrict__ bitmask,
@@ -584,6 +500,12 @@ __global__ __launch_bounds__(256) void k_csr(const int32_t *__restrict__ counts,
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int b = blockIdx.x;
   const int r0 = b * 64;
+  uint32_t wv[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int rk = r0 + 16 * w + k;
+    wv[k] = (rk < rows && lane < nkw) ? bitmask[(size_t)rk * nkw + lane] : 0u;
+  }
   int part = 0;
   for (int i = tid; i < b; i += 256) part += bsum[i];
 #pragma unroll
@@ -607,17 +529,17 @@ __global__ __launch_bounds__(256) void k_csr(const int32_t *__restrict__ counts,
   }
   __syncthreads();
   const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int nch = (nkb + 63) >> 6;
+#pragma unroll
   for (int k = 0; k < 16; ++k) {
     const int rk = r0 + 16 * w + k;
     if (rk >= rows) break;
     int out = s_rp[16 * w + k];
-    const uint32_t *bm = bitmask + (size_t)rk * nkw;
-    for (int j0 = 0; j0 < nkb; j0 += 64) {
-      const int j = j0 + lane;
-      const bool kept = j < nkb && ((bm[j >> 5] >> (j & 31)) & 1u);
-      const unsigned long long bal = __ballot(kept);
-      if (kept) col_idx[out + __popcll(bal & lt)] = j;
-      out += __popcll(bal);
+    for (int c = 0; c < nch; ++c) {
+      const unsigned long long mask = (unsigned long long)(uint32_t)__shfl((int)wv[k], 2 * c) |
+                                      ((unsigned long long)(uint32_t)__shfl((int)wv[k], 2 * c + 1) << 32);
+      if ((mask >> lane) & 1ull) col_idx[out + __popcll(mask & lt)] = 64 * c + lane;
+      out += __popcll(mask);
     }
   }
 }
