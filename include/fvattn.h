@@ -256,8 +256,9 @@ int fvattn_sparse_attn(const void *q, const void *k, const void *v, void *o, int
 
 /*
  * First half of fvattn_sparse_attn: builds the work list of the CSR rows in `schedule`
- * order and, for bf16, the transposed copy of v the attention kernel stages from, all in
- * `ws`.  The plan stays valid while v, the CSR and ws are unchanged.
+ * order and, for bf16 with 32-token key blocks, the transposed copy of v that kernel stages
+ * from, all in `ws` (with 64-token key blocks the attention kernel reads v as given).  The plan
+ * stays valid while v, the CSR and ws are unchanged.
  */
 int fvattn_attn_plan(const void *v, int B, int H, int N, int d, int dtype, const fvattn_csr *csr,
                      int schedule, void *ws, size_t ws_bytes, void *stream);

@@ -61,9 +61,11 @@ def test_sizes(L):
     assert L.fvattn_csr_max_nnz(1, 1, 100, 48, 64) == UNSUPPORTED
     assert L.fvattn_route_ws_bytes(1, 40, 32760, 128, 64, 64) > 2 * 40 * 512 * 128 * 8
     assert L.fvattn_route_ws_bytes(1, 40, 32760, 96, 64, 64) == 0
+    # bf16 with 32-key blocks also holds a transposed copy of V; 64-key blocks read V as given
     bf = L.fvattn_attn_ws_bytes(1, 40, 32760, 128, 0, 64, 64)
+    bf32 = L.fvattn_attn_ws_bytes(1, 40, 32760, 128, 0, 64, 32)
     f32 = L.fvattn_attn_ws_bytes(1, 40, 32760, 128, 1, 64, 64)
-    assert bf >= 40 * 128 * 32768 * 2 > f32 > 0
+    assert bf32 >= 40 * 128 * 32768 * 2 > bf == f32 > 0
     assert L.fvattn_attn_ws_bytes(1, 40, 32760, 128, 7, 64, 64) == 0
 
 

@@ -76,6 +76,10 @@ SMALL = [
                                                             "f32", (7, 10, 10)), 0.9),
     ("bf16_h2_n40_short", lambda: workloads.small_case(2, 40, 128, 64, 64, 26, ("uniform", 0.0, 3.0),
                                                        "bf16", (1, 5, 8)), 0.5),
+    ("bf16_h2_n2100_d64", lambda: workloads.small_case(2, 2100, 64, 64, 64, 28, ("uniform", 0.0, 3.0),
+                                                       "bf16", (5, 20, 21)), 0.9),
+    ("bf16_h2_n1800_bq32", lambda: workloads.small_case(2, 1800, 128, 32, 64, 29, ("uniform", 0.5, 3.0),
+                                                        "bf16", (3, 20, 30)), 0.85),
     ("bf16_h1_n75600_nkb1182", lambda: workloads.small_case(1, 75600, 128, 64, 64, 27, ("uniform", 0.0, 3.0),
                                                             "bf16", (21, 45, 80)), 0.9),
 ]

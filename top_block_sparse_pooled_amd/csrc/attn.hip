@@ -281,6 +281,8 @@ struct AttnCfg {
 };
 
 typedef __attribute__((address_space(3))) void *lds_void_ptr;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 *lds_v4i16_ptr;
 
 // Raw buffer resource over `bytes` bytes at `base`: loads past the end return zero.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, uint32_t bytes) {
@@ -646,7 +648,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 template <int BQ, int BK, int D>
 __global__ __launch_bounds__(512, 1) void k_attn_pp(
-    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ vt,
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     void *__restrict__ o, int out_f32, const int32_t *__restrict__ row_ptr, const int32_t *__restrict__ col_idx,
     const int32_t *__restrict__ worklist, int32_t *__restrict__ counter, int units, int ngroups, int nqb, int N,
     int NKP, float sl2, uint64_t *__restrict__ trace) {
@@ -675,18 +677,30 @@ __global__ __launch_bounds__(512, 1) void k_attn_pp(
   const int l32 = lane & 31, h = lane >> 5;
 
   const int k_r0 = lane / C::KCR, k_pos = lane % C::KCR;
-  const int v_r0 = lane / C::VCR, v_pos = lane % C::VCR;
-  uint32_t k_vo[C::KPER], v_vo[C::VPER];
+  uint32_t k_vo[C::KPER];
 #pragma unroll
   for (int j = 0; j < C::KPER; ++j) {
     const int r = j * C::KRPI + k_r0;
     k_vo[j] = (uint32_t)(k_r0 * C::KROW + swz_pos(k_pos, r, C::KROW, C::KCR) * 16);
   }
+  // V tiles keep V's own layout (one key per row of 2D bytes).  The 16-byte chunk c of key row
+  // r sits at chunk position c ^ (vsw(r) << 2), vsw(r) = r & 3 for d = 128 and (r >> 1) & 1 for
+  // d = 64: the eight key rows that one transposing read of the P.V operand touches then fall
+  // on all banks twice.  Each 1 KB load covers whole rows starting at a multiple of 4 (d = 128)
+  // or 8 (d = 64), so vsw depends only on the lane.
+  const int v_sw = D == 128 ? (k_r0 & 3) : ((k_r0 >> 1) & 1);
+  const uint32_t v_vo = (uint32_t)(k_r0 * C::KROW + ((k_pos ^ (v_sw << 2)) * 16));
+  // P.V operand reads: in each 16-lane group, lane a supplies dims 4(a & 3) .. +3 (of the
+  // group's 16) of key row a >> 2, and the transposing read hands every lane the 4 keys of
+  // its own dim.  Read 1 covers keys 16 kk + 4 h + 0..3, read 2 the same + 8: the key order of
+  // the P fragment taken from the S accumulator.  tr_off[m]: byte offset for output tile m.
+  const int tra = lane & 15, trg = (lane >> 4) & 1;
+  const int tr_sw = D == 128 ? (tra >> 2) : ((tra >> 3) & 1);
+  uint32_t tr_off[C::NM];
 #pragma unroll
-  for (int j = 0; j < C::VPER; ++j) {
-    const int r = j * C::VRPI + v_r0;
-    v_vo[j] = (uint32_t)(v_r0 * NKP * 2 + swz_pos(v_pos, r, C::VROW, C::VCR) * 16);
-  }
+  for (int m = 0; m < C::NM; ++m)
+    tr_off[m] = (uint32_t)((4 * h + (tra >> 2)) * C::KROW + (4 * (m ^ tr_sw) + 2 * trg + ((tra & 3) >> 1)) * 16 +
+                           8 * (tra & 1));
 
   const bool per_xcd = counter[2] != 0;
   const int xcc = (int)(__builtin_amdgcn_s_getreg((31 << 11) | 20) & 7);   // XCC_ID
@@ -719,9 +733,9 @@ __global__ __launch_bounds__(512, 1) void k_attn_pp(
     const int r0 = bh * nqb + g * G;
     const int nrow = min(G, nqb - g * G);
     const uint16_t *kh = k + (size_t)bh * N * D;
-    const uint16_t *vth = vt + (size_t)bh * D * NKP;
+    const uint16_t *vh = v + (size_t)bh * N * D;
     const __amdgpu_buffer_rsrc_t krs = buf_rsrc(kh, (uint32_t)N * D * 2);
-    const __amdgpu_buffer_rsrc_t vrs = buf_rsrc(vth, (uint32_t)D * NKP * 2);
+    const __amdgpu_buffer_rsrc_t vrs = buf_rsrc(vh, (uint32_t)N * D * 2);
     // Tile loads of this group.  A negative block index loads from far outside the buffer:
     // the range check returns zeros without touching memory, so every X phase issues the same
     // number of loads and the vmcnt waits stay static.
@@ -742,19 +756,10 @@ __global__ __launch_bounds__(512, 1) void k_attn_pp(
       }
     };
     auto load_v = [&](int jb, uint8_t *vbuf) {
-      const uint32_t sbase = jb < 0 ? kFar : (uint32_t)jb * BK * 2 + (uint32_t)wg * C::VI * C::VRPI * NKP * 2;
-      uint8_t *dst = vbuf + wg * C::VI * 1024;
+      const uint32_t sbase = jb < 0 ? kFar : (uint32_t)jb * BK * D * 2 + (uint32_t)wg * C::KI * C::KRPI * C::KROW;
+      uint8_t *dst = vbuf + wg * C::KI * 1024;
 #pragma unroll
-      for (int i = 0; i < C::VI; ++i) {
-        uint32_t vo;
-        if constexpr (C::VTAB) {
-          vo = v_vo[i % C::VPER];
-        } else {
-          const int gi = wg * C::VI + i;
-          vo = (uint32_t)(v_r0 * NKP * 2 + swz_pos(v_pos, gi * C::VRPI + v_r0, C::VROW, C::VCR) * 16);
-        }
-        dma16(vrs, vo + sbase + (uint32_t)i * C::VRPI * NKP * 2, 0, dst + i * 1024);
-      }
+      for (int i = 0; i < C::KI; ++i) dma16(vrs, v_vo + sbase + (uint32_t)i * C::KRPI * C::KROW, 0, dst + i * 1024);
     };
 
     // this wave's query rows; loaded first, so the
@@ -879,20 +884,22 @@ __global__ __launch_bounds__(512, 1) void k_attn_pp(
       }
       if (dop) {
         constexpr int NT_P = C::NKT * 2 * C::NM;   // MFMA t: (kt, t2) = t / NM, output tile t % NM
-        auto vaddr = [&](int t) {
+        auto vfrag = [&](int t) -> bf16x8 {
           const int kk = t / C::NM, m = t % C::NM;
-          return reinterpret_cast<const bf16x8 *>(vbp + (32 * m + l32) * C::VROW +
-                                                  swz_pos(2 * kk + h, l32, C::VROW, C::VCR) * 16);
+          const uint8_t *p0 = vbp + tr_off[m] + 16 * kk * C::KROW;
+          const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)p0);
+          const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(p0 + 8 * C::KROW));
+          return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         };
         bf16x8 fr[RING];
 #pragma unroll
-        for (int t = 0; t < RING; ++t) fr[t] = *vaddr(t);
+        for (int t = 0; t < RING; ++t) fr[t] = vfrag(t);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int t = 0; t < NT_P; ++t) {
           const int kk = t / C::NM;
           oacc[t % C::NM] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[t % RING], pf[kk >> 1][kk & 1], oacc[t % C::NM], 0, 0, 0);
-          if (t + RING < NT_P) fr[t % RING] = *vaddr(t + RING);
+          if (t + RING < NT_P) fr[t % RING] = vfrag(t + RING);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -1141,10 +1148,11 @@ int launch_worklist(const int32_t *row_ptr, int rows, int nqb, int nkb, int G, i
 }
 
 template <int BQ, int BK, int D>
-static int launch_attn_bf16_t(const void *q, const void *k, const void *vt, void *o, int out_f32,
+static int launch_attn_bf16_t(const void *q, const void *k, const void *v, const void *vt, void *o, int out_f32,
                               const int32_t *row_ptr, const int32_t *col_idx, const int32_t *wl, int32_t *counter,
                               int rows, int nqb, int N, int NKP, int grid, uint64_t *trace, hipStream_t st) {
-  // 64-key blocks: two wave groups per unit (k_attn_pp); 32-key blocks: k_attn_bf16
+  // 64-key blocks: two wave groups per unit (k_attn_pp), V as given; 32-key blocks: k_attn_bf16
+  // over the transposed copy of V
   auto kern = BK == 64 ? k_attn_pp<BQ, 64, D> : k_attn_bf16<BQ, BK, D>;
   const int nthreads = BK == 64 ? 512 : 256;
   constexpr int G = 128 / BQ;
@@ -1159,18 +1167,20 @@ static int launch_attn_bf16_t(const void *q, const void *k, const void *vt, void
   if (grid > units) grid = units;
   const float sl2 = (float)(1.4426950408889634 / sqrt((double)D));
   hipLaunchKernelGGL(kern, dim3(grid), dim3(nthreads), 0, st, (const uint16_t *)q, (const uint16_t *)k,
-                     (const uint16_t *)vt, o, out_f32, row_ptr, col_idx, wl, counter, units, ngroups, nqb, N, NKP,
+                     (const uint16_t *)(BK == 64 ? v : vt), o, out_f32, row_ptr, col_idx, wl, counter, units, ngroups,
+                     nqb, N, NKP,
                      sl2, trace);
   FV_CHECK_LAUNCH();
   return FVATTN_OK;
 }
 
-int launch_attn_bf16(const void *q, const void *k, const void *vt, void *o, int out_f32, const int32_t *row_ptr,
+int launch_attn_bf16(const void *q, const void *k, const void *v, const void *vt, void *o, int out_f32,
+                     const int32_t *row_ptr,
                      const int32_t *col_idx, const int32_t *wl, int32_t *counter, int rows, int nqb, int N, int NKP,
                      int D, int BQ, int BK, int grid, uint64_t *trace, hipStream_t st) {
 #define FV_A(bq, bk, dd)                                                                                 \
   if (BQ == bq && BK == bk && D == dd)                                                                   \
-    return launch_attn_bf16_t<bq, bk, dd>(q, k, vt, o, out_f32, row_ptr, col_idx, wl, counter, rows, nqb, N, \
+    return launch_attn_bf16_t<bq, bk, dd>(q, k, v, vt, o, out_f32, row_ptr, col_idx, wl, counter, rows, nqb, N, \
                                           NKP, grid, trace, st);
   FV_A(64, 64, 128) FV_A(128, 64, 128) FV_A(32, 64, 128) FV_A(64, 32, 128) FV_A(128, 32, 128) FV_A(32, 32, 128)
   FV_A(64, 64, 64) FV_A(128, 64, 64) FV_A(32, 64, 64) FV_A(64, 32, 64) FV_A(128, 32, 64) FV_A(32, 32, 64)

@@ -287,6 +287,7 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 ? 2 : 1) void k_select(const dou
   __shared__ double s_part[NWV][16];
   __shared__ unsigned long long s_zpart[NWV][16];
   __shared__ double s_minpart[NWV][16];
+  __shared__ int s_cnt[16];           // kept counts of the item's rows
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -412,7 +413,10 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 ? 2 : 1) void k_select(const dou
     for (int rr = 0; rr < RPW; ++rr) {
       const int r = b * RB + rr * NWV + w;
       const int i = 16 * g + r;
-      if (i >= nqb) continue;   // wave-uniform
+      if (i >= nqb) {   // wave-uniform
+        if (lane == 0) s_cnt[r] = 0;
+        continue;
+      }
       const size_t row = (size_t)bh * nqb + i;
       double ev[NPL];
 #pragma unroll
@@ -467,8 +471,7 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 ? 2 : 1) void k_select(const dou
       if (lane < nkw) bitmask[row * nkw + lane] = word;
       if (lane == 0) {
         counts[row] = c;
-        atomicAdd(&head_load[bh], c);
-        atomicAdd(&bsum[row >> 6], c);   // per-64-row sums for the CSR scan
+        s_cnt[r] = c;
       }
       if (EXT && sel.imp != nullptr) {
         // importance of every block: the candidates' order for SASA
@@ -479,6 +482,24 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 ? 2 : 1) void k_select(const dou
       }
     }
     __syncthreads();   // staged rows and partial sums consumed before they are overwritten
+  }
+  if (w == 0) {
+    // the item's load of the head and its per-64-row sums for the CSR scan (the 16 rows
+    // span at most two 64-row blocks)
+    const size_t row0 = (size_t)bh * nqb + 16 * g;
+    const int c = lane < 16 ? s_cnt[lane] : 0;
+    const bool second = lane < 16 && ((row0 + lane) >> 6) != (row0 >> 6);
+    int c0 = second ? 0 : c, c1 = second ? c : 0;
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) {
+      c0 += __shfl_xor(c0, off);
+      c1 += __shfl_xor(c1, off);
+    }
+    if (lane == 0) {
+      atomicAdd(&head_load[bh], c0 + c1);
+      atomicAdd(&bsum[row0 >> 6], c0);
+      if (c1 != 0) atomicAdd(&bsum[(row0 >> 6) + 1], c1);
+    }
   }
   }
 }
