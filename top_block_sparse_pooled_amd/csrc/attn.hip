@@ -294,6 +294,14 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, u
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_ptr)lds_dst, 16, voff, soff, 0, 0);
 }
 
+// The same with an instruction offset OFF, which the hardware adds to both the buffer address
+// and the LDS address: consecutive 1 KB pieces of a tile then share one LDS base (M0).
+template <int OFF>
+__device__ __forceinline__ void dma16_at(__amdgpu_buffer_rsrc_t r, uint32_t voff, void *lds_dst) {
+  static_assert(OFF >= 0 && OFF < 4096, "12-bit instruction offset");
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_ptr)lds_dst, 16, voff, 0, OFF, 0);
+}
+
 // 16-byte chunk position of chunk c in row r of a swizzled tile (rows of `rowbytes` bytes,
 // `cr` chunks per row): rows that share a 256-byte bank line get different XOR keys.
 __host__ __device__ constexpr int swz_pos(int c, int r, int rowbytes, int cr) {
@@ -740,11 +748,14 @@ __global__ __launch_bounds__(512, 1) void k_attn_pp(
     // the range check returns zeros without touching memory, so every X phase issues the same
     // number of loads and the vmcnt waits stay static.
     constexpr uint32_t kFar = 0x7fff0000u;
+    // Piece i of a wave's part is 1 KB further in both the tile and LDS, so all pieces use the
+    // part's LDS base with instruction offsets 1024 i.
+    static_assert(C::KRPI * C::KROW == 1024 && C::KI * 1024 <= 4096, "1 KB pieces, 12-bit offsets");
     auto load_k = [&](int jb, uint8_t *kbuf) {
       const uint32_t sbase = jb < 0 ? kFar : (uint32_t)jb * BK * D * 2 + (uint32_t)wg * C::KI * C::KRPI * C::KROW;
       uint8_t *dst = kbuf + wg * C::KI * 1024;
-#pragma unroll
-      for (int i = 0; i < C::KI; ++i) {
+      auto piece = [&](auto ic) {
+        constexpr int i = decltype(ic)::value;
         uint32_t vo;
         if constexpr (C::KTAB) {
           vo = k_vo[i % C::KPER];
@@ -752,14 +763,20 @@ __global__ __launch_bounds__(512, 1) void k_attn_pp(
           const int gi = wg * C::KI + i;
           vo = (uint32_t)(k_r0 * C::KROW + swz_pos(k_pos, gi * C::KRPI + k_r0, C::KROW, C::KCR) * 16);
         }
-        dma16(krs, vo + sbase + (uint32_t)i * C::KRPI * C::KROW, 0, dst + i * 1024);
-      }
+        dma16_at<i * 1024>(krs, vo + sbase, dst);
+      };
+      piece(std::integral_constant<int, 0>{});
+      if constexpr (C::KI > 1) piece(std::integral_constant<int, 1>{});
+      if constexpr (C::KI > 2) piece(std::integral_constant<int, 2>{});
+      if constexpr (C::KI > 3) piece(std::integral_constant<int, 3>{});
     };
     auto load_v = [&](int jb, uint8_t *vbuf) {
       const uint32_t sbase = jb < 0 ? kFar : (uint32_t)jb * BK * D * 2 + (uint32_t)wg * C::KI * C::KRPI * C::KROW;
       uint8_t *dst = vbuf + wg * C::KI * 1024;
-#pragma unroll
-      for (int i = 0; i < C::KI; ++i) dma16(vrs, v_vo + sbase + (uint32_t)i * C::KRPI * C::KROW, 0, dst + i * 1024);
+      dma16_at<0>(vrs, v_vo + sbase, dst);
+      if constexpr (C::KI > 1) dma16_at<1024>(vrs, v_vo + sbase, dst);
+      if constexpr (C::KI > 2) dma16_at<2048>(vrs, v_vo + sbase, dst);
+      if constexpr (C::KI > 3) dma16_at<3072>(vrs, v_vo + sbase, dst);
     };
 
     // this wave's query rows; loaded first, so the
