@@ -7,14 +7,13 @@
 
 namespace fv {
 int launch_pool(const void *x, int BH, int N, int d, int dtype, int block, double *out, hipStream_t st);
-int launch_pool_qk(const void *q, const void *k, int BH, int N, int d, int dtype, int block_q, int block_k,
-                   double *qsw, double *ksw, int32_t *zero0, int nzero0, int32_t *zero1, int nzero1,
-                   hipStream_t st);
+int launch_pool_k(const void *k, int BH, int N, int d, int dtype, int block_k, double *ksw, int32_t *zero0, int nzero0,
+                  int32_t *zero1, int nzero1, hipStream_t st);
 size_t sasa_group_bytes(int R);
 int launch_sasa(const double *imp, uint32_t *bitmask, int32_t *counts, int32_t *bsum, int32_t *head_load, int nkw,
                 int nqb, int nkb, int BH, int R, int critical, double alpha, double tau, void *grp_buf,
                 uint32_t *ghist, int32_t *tiecnt, int32_t *tiepre, int32_t *added_out, hipStream_t st);
-int launch_select(const double *qsw, const double *ksw, int BH, int d, int nqb, int nkb, double p,
+int launch_select(const void *q, const double *ksw, int BH, int d, int dtype, int nqb, int nkb, double p,
                   int32_t *counts, uint32_t *bitmask, int nkw, int32_t *head_load, int32_t *bsum, int mode, int topk,
                   int k_min, int k_max, int window, int bq, int bk, int N, double *imp, hipStream_t st);
 int launch_csr(const int32_t *counts, const uint32_t *bitmask, const int32_t *bsum, int rows, int nkw, int nkb,
@@ -63,7 +62,7 @@ int check_shape(int B, int H, int N, int d, int bq, int bk, Shape *s) {
 }
 
 struct RouteWs {
-  double *qsw, *ksw;
+  double *ksw;      // pooled K (the query blocks are pooled inside the select kernel)
   int32_t *counts;
   uint32_t *bitmask;
   int32_t *bsum;   // per-64-row sums of counts
@@ -74,8 +73,6 @@ struct RouteWs {
 RouteWs route_ws_layout(const Shape &s, char *base) {
   RouteWs w;
   size_t off = 0;
-  w.qsw = (double *)(base + off);
-  off += align256((size_t)s.BH * s.nqbp * s.d * sizeof(double));
   w.ksw = (double *)(base + off);
   off += align256((size_t)s.BH * s.nkbp * s.d * sizeof(double));
   w.counts = (int32_t *)(base + off);
@@ -212,11 +209,11 @@ int route_core(const void *q, const void *k, const Shape &s, int N, int d, int d
                hipStream_t st) {
   int rc;
   csr->bh = s.BH; csr->n = N; csr->block_q = block_q; csr->block_k = block_k; csr->nqb = s.nqb; csr->nkb = s.nkb;
-  if ((rc = fv::launch_pool_qk(q, k, s.BH, N, d, dtype, block_q, block_k, w.qsw, w.ksw, w.bsum, w.nblk,
-                               csr->head_load, s.BH, st)) != FVATTN_OK)
+  if ((rc = fv::launch_pool_k(k, s.BH, N, d, dtype, block_k, w.ksw, w.bsum, w.nblk, csr->head_load, s.BH, st)) !=
+      FVATTN_OK)
     return rc;
   const double p = o.mode == FVATTN_ROUTE_TOPP ? o.p : 1.0;
-  if ((rc = fv::launch_select(w.qsw, w.ksw, s.BH, d, s.nqb, s.nkb, p, w.counts, w.bitmask, s.nkw, csr->head_load,
+  if ((rc = fv::launch_select(q, w.ksw, s.BH, d, dtype, s.nqb, s.nkb, p, w.counts, w.bitmask, s.nkw, csr->head_load,
                               w.bsum, o.mode, o.topk, o.k_min, o.k_max, o.window, block_q, block_k, N, imp, st)) !=
       FVATTN_OK)
     return rc;

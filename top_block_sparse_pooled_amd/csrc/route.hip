@@ -54,13 +54,56 @@ struct PoolArgs {
   int nzero[2];
 };
 
+// Mean of the real tokens of block j (tokens [j block, min(j block + block, N))) of one head's
+// rows xh, by one wave: lane l reads 16-byte chunk l % CPR of rows l / CPR + RPL i (16 loads
+// in flight per lane), accumulates in float64, and the lanes of a chunk are summed with
+// cross-lane shuffles.  Lanes l < CPR return dims l EPC .. l EPC + EPC - 1 (zero for j >= nb).
 template <typename T, int D>
-__global__ __launch_bounds__(256) void k_pool(PoolArgs a) {
+__device__ __forceinline__ void pool_block(const T *__restrict__ xh, int j, int block, int nb, int N,
+                                           double (&mean)[DT<T>::per16]) {
   constexpr int EPC = DT<T>::per16;   // elements per 16-byte chunk
   constexpr int CPR = D / EPC;        // chunks per row
   constexpr int RPL = 64 / CPR;       // rows covered by one wave-wide load
   constexpr int NLD = 16;             // loads in flight per lane
   constexpr int RPR = RPL * NLD;      // rows per round
+  const int lane = threadIdx.x & 63;
+  const int c = lane % CPR, r = lane / CPR;
+  double acc[EPC];
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) acc[e] = 0.0;
+  int cnt = 1;
+  if (j < nb) {
+    const int s0 = j * block, e0 = min(s0 + block, N);
+    cnt = e0 - s0;
+    for (int base = s0; base < e0; base += RPR) {
+      u32x4 buf[NLD];
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) {
+        const int row = base + r + RPL * i;
+        buf[i] = u32x4{0u, 0u, 0u, 0u};
+        if (row < e0) buf[i] = *reinterpret_cast<const u32x4 *>(xh + (size_t)row * D + c * EPC);
+      }
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) {
+        float f[EPC];
+        unpack16(buf[i], f, T());
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) acc[e] += (double)f[e];
+      }
+    }
+  }
+#pragma unroll
+  for (int off = CPR; off < 64; off <<= 1)
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) acc[e] += __shfl_xor(acc[e], off);
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) mean[e] = (j < nb) ? acc[e] / (double)cnt : 0.0;
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_pool(PoolArgs a) {
+  constexpr int EPC = DT<T>::per16;   // elements per 16-byte chunk
+  constexpr int CPR = D / EPC;        // chunks per row
   __shared__ double stage[16][D + 1];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -75,41 +118,13 @@ __global__ __launch_bounds__(256) void k_pool(PoolArgs a) {
   }
   const T *xh = reinterpret_cast<const T *>(a.x[t]) + (size_t)bh * a.N * D;
   const int block = a.block[t], nb = a.nb[t], N = a.N;
-  const int c = lane % CPR, r = lane / CPR;
 
   for (int jj = w; jj < 16; jj += 4) {
-    const int j = gx * 16 + jj;
-    double acc[EPC];
+    double m[EPC];
+    pool_block<T, D>(xh, gx * 16 + jj, block, nb, N, m);
+    if (lane < CPR) {
 #pragma unroll
-    for (int e = 0; e < EPC; ++e) acc[e] = 0.0;
-    int cnt = 1;
-    if (j < nb) {
-      const int s0 = j * block, e0 = min(s0 + block, N);
-      cnt = e0 - s0;
-      for (int base = s0; base < e0; base += RPR) {
-        u32x4 buf[NLD];
-#pragma unroll
-        for (int i = 0; i < NLD; ++i) {
-          const int row = base + r + RPL * i;
-          buf[i] = u32x4{0u, 0u, 0u, 0u};
-          if (row < e0) buf[i] = *reinterpret_cast<const u32x4 *>(xh + (size_t)row * D + c * EPC);
-        }
-#pragma unroll
-        for (int i = 0; i < NLD; ++i) {
-          float f[EPC];
-          unpack16(buf[i], f, T());
-#pragma unroll
-          for (int e = 0; e < EPC; ++e) acc[e] += (double)f[e];
-        }
-      }
-    }
-#pragma unroll
-    for (int off = CPR; off < 64; off <<= 1)
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) acc[e] += __shfl_xor(acc[e], off);
-    if (r == 0) {
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) stage[jj][c * EPC + e] = (j < nb) ? acc[e] / (double)cnt : 0.0;
+      for (int e = 0; e < EPC; ++e) stage[jj][lane * EPC + e] = m[e];
     }
   }
   __syncthreads();
@@ -267,8 +282,8 @@ __device__ __forceinline__ uint32_t select_row(const double (&ev)[NPL], int nkb,
   return word;
 }
 
-template <int D, int MAXT, int NWV, bool EXT>
-__global__ __launch_bounds__(64 * NWV, NWV == 4 ? 2 : 1) void k_select(const double *__restrict__ qsw,
+template <typename T, int D, int MAXT, int NWV, bool EXT>
+__global__ __launch_bounds__(64 * NWV, NWV == 4 ? 2 : 1) void k_select(const void *__restrict__ qraw,
                                                 const double *__restrict__ ksw, int nqb, int nkb,
                                                 double scale, double p, int32_t *__restrict__ counts,
                                                 uint32_t *__restrict__ bitmask, int nkw,
@@ -281,7 +296,11 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 ? 2 : 1) void k_select(const dou
   constexpr int NB = 16 / RB;
   constexpr int RPW = RB / NWV;           // rows per wave per batch
   static_assert(KCAP % 64 == 0 && RB % NWV == 0 && (RB / 4) * 4 == RB, "row phase geometry");
-  __shared__ double s_e[RB][KCAP];
+  constexpr int EPC = DT<T>::per16, CPR = D / EPC;
+  // staged rows; before them, the item's pooled query blocks (16 D doubles)
+  constexpr int ESZ = RB * KCAP > 16 * D ? RB * KCAP : 16 * D;
+  __shared__ double s_eq[ESZ];
+  double(*s_e)[KCAP] = reinterpret_cast<double(*)[KCAP]>(s_eq);
   __shared__ unsigned long long h_mass[NWV][256];
   __shared__ uint32_t h_cnt[NWV][256];
   __shared__ double s_part[NWV][16];
@@ -304,17 +323,36 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 ? 2 : 1) void k_select(const dou
   for (int it = (int)((long long)items * xcd / 8) + (int)(blockIdx.x >> 3); it < it_end; it += nwx) {
   const int bh = it / nqg, g = it - bh * nqg;
 
+  // ---- the item's 16 query blocks, mean-pooled straight into LDS in the float64 MFMA
+  // operand order (block jj, dim c at (c / 4) 64 + jj + 16 (c % 4)); the raw Q reads of one
+  // workgroup overlap the score phases of the others
+  {
+    const T *xh = reinterpret_cast<const T *>(qraw) + (size_t)bh * sel.N * D;
+    for (int jj = w; jj < 16; jj += NWV) {
+      double m[EPC];
+      pool_block<T, D>(xh, 16 * g + jj, sel.bq, nqb, sel.N, m);
+      if (lane < CPR) {
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) {
+          const int cc = lane * EPC + e;
+          s_eq[(cc >> 2) * 64 + jj + 16 * (cc & 3)] = m[e];
+        }
+      }
+    }
+  }
+  __syncthreads();
+
   // ---- scores: S[i][j] = sum_c qbar[i][c] * kbar[j][c], i = lane/16 + 4v, j = 16t + lane%16
   d4 acc[MAXT];
 #pragma unroll
   for (int k = 0; k < MAXT; ++k) acc[k] = d4{0.0, 0.0, 0.0, 0.0};
   {
-    const double *qa = qsw + ((size_t)(bh * nqg + g) * KS) * 64 + lane;
+    const double *qa = s_eq + lane;
     // k-step outer, tiles inner: MAXT independent accumulators.  The operands of PF k-steps
     // (one of qbar, MAXT of kbar each) are in flight ahead of the MFMAs that use them, which
     // covers the L2 latency of the pooled keys.  Tiles past the last read a valid tile (their
     // key columns are >= nkb and ignored below), so the loop has no branches.
-    constexpr int PF = MAXT >= 10 ? 1 : (MAXT >= 8 ? 2 : 3);
+    constexpr int PF = MAXT >= 8 ? 1 : 3;
     const double *kb[MAXT];
 #pragma unroll
     for (int k = 0; k < MAXT; ++k) kb[k] = ksw + ((size_t)(bh * nkt + min(w + NWV * k, nkt - 1)) * KS) * 64 + lane;
@@ -431,21 +469,21 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 ? 2 : 1) void k_select(const dou
       const unsigned long long lo0 = (unsigned long long)__double_as_longlong(emin);
       // search by mass (Top-p) or by count (top-k, or a clamped Top-p count)
       bool bycnt = false;
-      unsigned long long T;
+      unsigned long long tgt0;
       bool all;
       if (EXT && sel.mode == FVATTN_ROUTE_TOPK) {
         bycnt = true;
-        T = (unsigned long long)sel.topk;
+        tgt0 = (unsigned long long)sel.topk;
         all = sel.topk >= nkb;
       } else {
-        T = (unsigned long long)ceil(p * (double)Z);
-        if (T > Z) T = Z;
-        if (T < 1) T = 1;
+        tgt0 = (unsigned long long)ceil(p * (double)Z);
+        if (tgt0 > Z) tgt0 = Z;
+        if (tgt0 < 1) tgt0 = 1;
         all = p >= 1.0;
       }
       int c;
       // lane L < nkw holds kept word L (key blocks 32 L .. 32 L + 31)
-      uint32_t word = select_row<NPL>(ev, nkb, bycnt, T, lo0, all, h_mass[w], h_cnt[w], c);
+      uint32_t word = select_row<NPL>(ev, nkb, bycnt, tgt0, lo0, all, h_mass[w], h_cnt[w], c);
       if (EXT && !bycnt && (sel.k_min > 1 || sel.k_max > 0)) {
         // clamp of the Top-p count: re-select by count when it lies outside [k_min, k_max]
         int tgt = max(c, sel.k_min);
@@ -593,20 +631,16 @@ int launch_pool(const void *x, int BH, int N, int d, int dtype, int block, doubl
   return launch_pool_args(pa, BH, d, dtype, st);
 }
 
-int launch_pool_qk(const void *q, const void *k, int BH, int N, int d, int dtype, int block_q, int block_k,
-                   double *qsw, double *ksw, int32_t *zero0, int nzero0, int32_t *zero1, int nzero1,
-                   hipStream_t st) {
+// Pooled K in the float64 MFMA operand order of k_select (the query blocks are pooled inside
+// k_select), and the zeroing of the two counter arrays (per-64-row sums, head loads).
+int launch_pool_k(const void *k, int BH, int N, int d, int dtype, int block_k, double *ksw, int32_t *zero0, int nzero0,
+                  int32_t *zero1, int nzero1, hipStream_t st) {
   PoolArgs pa = {};
-  pa.x[0] = q;
-  pa.x[1] = k;
-  pa.out[0] = qsw;
-  pa.out[1] = ksw;
-  pa.block[0] = block_q;
-  pa.block[1] = block_k;
-  for (int t = 0; t < 2; ++t) {
-    pa.nb[t] = cdiv(N, pa.block[t]);
-    pa.ngrp[t] = cdiv(pa.nb[t], 16);
-  }
+  pa.x[0] = k;
+  pa.out[0] = ksw;
+  pa.block[0] = block_k;
+  pa.nb[0] = cdiv(N, block_k);
+  pa.ngrp[0] = cdiv(pa.nb[0], 16);
   pa.N = N;
   pa.layout = 1;
   pa.zero[0] = zero0;
@@ -616,14 +650,14 @@ int launch_pool_qk(const void *q, const void *k, int BH, int N, int d, int dtype
   return launch_pool_args(pa, BH, d, dtype, st);
 }
 
-template <int D, int MT, int NWV>
-static int launch_select_mt(const double *qsw, const double *ksw, int BH, int nqb, int nkb, double p,
-                            int32_t *counts, uint32_t *bitmask, int nkw, int32_t *head_load, int32_t *bsum,
-                            const SelOpts &sel, hipStream_t st) {
+template <typename T, int D, int MT, int NWV>
+static int launch_select_mt(const void *q, const double *ksw, int BH, int nqb, int nkb, double p, int32_t *counts,
+                            uint32_t *bitmask, int nkw, int32_t *head_load, int32_t *bsum, const SelOpts &sel,
+                            hipStream_t st) {
   auto kern = (sel.mode != FVATTN_ROUTE_TOPP || sel.k_min > 1 || sel.k_max > 0 || sel.window > 0 ||
                sel.imp != nullptr)
-                  ? k_select<D, MT, NWV, true>
-                  : k_select<D, MT, NWV, false>;
+                  ? k_select<T, D, MT, NWV, true>
+                  : k_select<T, D, MT, NWV, false>;
   int cus = 0, occ = 0;
   if (device_cus(&cus) != 0) return FVATTN_ERR_HIP;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, 64 * NWV, 0) != hipSuccess) return FVATTN_ERR_HIP;
@@ -632,7 +666,7 @@ static int launch_select_mt(const double *qsw, const double *ksw, int BH, int nq
   if (grid > items) grid = items;
   if (grid < 8) grid = 8;   // every XCD range needs a worker
   const double scale = 1.0 / sqrt((double)D);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * NWV), 0, st, qsw, ksw, nqb, nkb, scale, p, counts, bitmask, nkw,
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * NWV), 0, st, q, ksw, nqb, nkb, scale, p, counts, bitmask, nkw,
                      head_load, bsum, BH, sel);
   FV_CHECK_LAUNCH();
   return FVATTN_OK;
@@ -640,13 +674,13 @@ static int launch_select_mt(const double *qsw, const double *ksw, int BH, int nq
 
 // Key tiles (of 16 blocks) per wave: up to 512 key blocks run on 4 waves with at most 8 tiles
 // each; more (up to 1280) on 8 waves with at most 10 tiles each.
-template <int D>
-static int launch_select_d(const double *qsw, const double *ksw, int BH, int nqb, int nkb, double p,
-                           int32_t *counts, uint32_t *bitmask, int nkw, int32_t *head_load, int32_t *bsum,
-                           const SelOpts &sel, hipStream_t st) {
+template <typename T, int D>
+static int launch_select_d(const void *q, const double *ksw, int BH, int nqb, int nkb, double p, int32_t *counts,
+                           uint32_t *bitmask, int nkw, int32_t *head_load, int32_t *bsum, const SelOpts &sel,
+                           hipStream_t st) {
   const int nkt = cdiv(nkb, 16);
 #define FV_SEL(MT, NWV) \
-  return launch_select_mt<D, MT, NWV>(qsw, ksw, BH, nqb, nkb, p, counts, bitmask, nkw, head_load, bsum, sel, st)
+  return launch_select_mt<T, D, MT, NWV>(q, ksw, BH, nqb, nkb, p, counts, bitmask, nkw, head_load, bsum, sel, st)
   if (nkt <= 4) FV_SEL(1, 4);
   if (nkt <= 8) FV_SEL(2, 4);
   if (nkt <= 16) FV_SEL(4, 4);
@@ -655,12 +689,18 @@ static int launch_select_d(const double *qsw, const double *ksw, int BH, int nqb
 #undef FV_SEL
 }
 
-int launch_select(const double *qsw, const double *ksw, int BH, int d, int nqb, int nkb, double p,
+int launch_select(const void *q, const double *ksw, int BH, int d, int dtype, int nqb, int nkb, double p,
                   int32_t *counts, uint32_t *bitmask, int nkw, int32_t *head_load, int32_t *bsum, int mode, int topk,
                   int k_min, int k_max, int window, int bq, int bk, int N, double *imp, hipStream_t st) {
   const SelOpts sel{mode, topk, k_min, k_max, window, bq, bk, N, imp};
-  if (d == 128) return launch_select_d<128>(qsw, ksw, BH, nqb, nkb, p, counts, bitmask, nkw, head_load, bsum, sel, st);
-  return launch_select_d<64>(qsw, ksw, BH, nqb, nkb, p, counts, bitmask, nkw, head_load, bsum, sel, st);
+  if (dtype == FVATTN_BF16) {
+    if (d == 128)
+      return launch_select_d<uint16_t, 128>(q, ksw, BH, nqb, nkb, p, counts, bitmask, nkw, head_load, bsum, sel, st);
+    return launch_select_d<uint16_t, 64>(q, ksw, BH, nqb, nkb, p, counts, bitmask, nkw, head_load, bsum, sel, st);
+  }
+  if (d == 128)
+    return launch_select_d<float, 128>(q, ksw, BH, nqb, nkb, p, counts, bitmask, nkw, head_load, bsum, sel, st);
+  return launch_select_d<float, 64>(q, ksw, BH, nqb, nkb, p, counts, bitmask, nkw, head_load, bsum, sel, st);
 }
 
 int launch_csr(const int32_t *counts, const uint32_t *bitmask, const int32_t *bsum, int rows, int nkw, int nkb,
