@@ -54,50 +54,61 @@ struct PoolArgs {
   int nzero[2];
 };
 
-// Mean of the real tokens of block j (tokens [j block, min(j block + block, N))) of one head's
-// rows xh, by one wave: lane l reads 16-byte chunk l % CPR of rows l / CPR + RPL i (16 loads
-// in flight per lane), accumulates in float64, and the lanes of a chunk are summed with
-// cross-lane shuffles.  Lanes l < CPR return dims l EPC .. l EPC + EPC - 1 (zero for j >= nb).
-template <typename T, int D>
-__device__ __forceinline__ void pool_block(const T *__restrict__ xh, int j, int block, int nb, int N,
-                                           double (&mean)[DT<T>::per16]) {
+// Means of the real tokens of NBK blocks j0, j0 + js, ... (block j: tokens [j block,
+// min(j block + block, N))) of one head's rows xh, by one wave: lane l reads 16-byte chunk
+// l % CPR of rows l / CPR + RPL i of every block (NBK x 16 loads in flight per lane),
+// accumulates in float64, and the lanes of a chunk are summed with cross-lane shuffles.  Lanes
+// l < CPR return dims l EPC .. l EPC + EPC - 1 of each block (zero for blocks >= nb).
+template <typename T, int D, int NBK>
+__device__ __forceinline__ void pool_blocks(const T *__restrict__ xh, int j0, int js, int block, int nb, int N,
+                                            double (&mean)[NBK][DT<T>::per16]) {
   constexpr int EPC = DT<T>::per16;   // elements per 16-byte chunk
   constexpr int CPR = D / EPC;        // chunks per row
   constexpr int RPL = 64 / CPR;       // rows covered by one wave-wide load
-  constexpr int NLD = 16;             // loads in flight per lane
+  constexpr int NLD = 16;             // loads in flight per lane and block
   constexpr int RPR = RPL * NLD;      // rows per round
   const int lane = threadIdx.x & 63;
   const int c = lane % CPR, r = lane / CPR;
-  double acc[EPC];
+  double acc[NBK][EPC];
+  int s0[NBK], e0[NBK];
 #pragma unroll
-  for (int e = 0; e < EPC; ++e) acc[e] = 0.0;
-  int cnt = 1;
-  if (j < nb) {
-    const int s0 = j * block, e0 = min(s0 + block, N);
-    cnt = e0 - s0;
-    for (int base = s0; base < e0; base += RPR) {
-      u32x4 buf[NLD];
+  for (int b = 0; b < NBK; ++b) {
+    const int j = j0 + b * js;
+    s0[b] = j < nb ? j * block : 0;
+    e0[b] = j < nb ? min(s0[b] + block, N) : 0;
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) acc[b][e] = 0.0;
+  }
+  for (int base = 0; base < block; base += RPR) {
+    u32x4 buf[NBK][NLD];
+#pragma unroll
+    for (int b = 0; b < NBK; ++b)
 #pragma unroll
       for (int i = 0; i < NLD; ++i) {
-        const int row = base + r + RPL * i;
-        buf[i] = u32x4{0u, 0u, 0u, 0u};
-        if (row < e0) buf[i] = *reinterpret_cast<const u32x4 *>(xh + (size_t)row * D + c * EPC);
+        const int row = s0[b] + base + r + RPL * i;
+        buf[b][i] = u32x4{0u, 0u, 0u, 0u};
+        if (row < e0[b]) buf[b][i] = *reinterpret_cast<const u32x4 *>(xh + (size_t)row * D + c * EPC);
       }
+#pragma unroll
+    for (int b = 0; b < NBK; ++b)
 #pragma unroll
       for (int i = 0; i < NLD; ++i) {
         float f[EPC];
-        unpack16(buf[i], f, T());
+        unpack16(buf[b][i], f, T());
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) acc[e] += (double)f[e];
+        for (int e = 0; e < EPC; ++e) acc[b][e] += (double)f[e];
       }
-    }
   }
 #pragma unroll
-  for (int off = CPR; off < 64; off <<= 1)
+  for (int b = 0; b < NBK; ++b) {
 #pragma unroll
-    for (int e = 0; e < EPC; ++e) acc[e] += __shfl_xor(acc[e], off);
+    for (int off = CPR; off < 64; off <<= 1)
 #pragma unroll
-  for (int e = 0; e < EPC; ++e) mean[e] = (j < nb) ? acc[e] / (double)cnt : 0.0;
+      for (int e = 0; e < EPC; ++e) acc[b][e] += __shfl_xor(acc[b][e], off);
+    const int cnt = e0[b] - s0[b];
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) mean[b][e] = cnt > 0 ? acc[b][e] / (double)cnt : 0.0;
+  }
 }
 
 template <typename T, int D>
@@ -120,11 +131,11 @@ __global__ __launch_bounds__(256) void k_pool(PoolArgs a) {
   const int block = a.block[t], nb = a.nb[t], N = a.N;
 
   for (int jj = w; jj < 16; jj += 4) {
-    double m[EPC];
-    pool_block<T, D>(xh, gx * 16 + jj, block, nb, N, m);
+    double m[1][EPC];
+    pool_blocks<T, D, 1>(xh, gx * 16 + jj, 0, block, nb, N, m);
     if (lane < CPR) {
 #pragma unroll
-      for (int e = 0; e < EPC; ++e) stage[jj][lane * EPC + e] = m[e];
+      for (int e = 0; e < EPC; ++e) stage[jj][lane * EPC + e] = m[0][e];
     }
   }
   __syncthreads();
@@ -328,15 +339,19 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 ? 2 : 1) void k_select(const voi
   // workgroup overlap the score phases of the others
   {
     const T *xh = reinterpret_cast<const T *>(qraw) + (size_t)bh * sel.N * D;
-    for (int jj = w; jj < 16; jj += NWV) {
-      double m[EPC];
-      pool_block<T, D>(xh, 16 * g + jj, sel.bq, nqb, sel.N, m);
+    // two blocks per wave at a time: 32 loads in flight per lane
+    constexpr int NBK = NWV == 4 ? 2 : 1;
+    for (int jj = w; jj < 16; jj += NBK * NWV) {
+      double m[NBK][EPC];
+      pool_blocks<T, D, NBK>(xh, 16 * g + jj, NWV, sel.bq, nqb, sel.N, m);
       if (lane < CPR) {
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) {
-          const int cc = lane * EPC + e;
-          s_eq[(cc >> 2) * 64 + jj + 16 * (cc & 3)] = m[e];
-        }
+        for (int b = 0; b < NBK; ++b)
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) {
+            const int cc = lane * EPC + e;
+            s_eq[(cc >> 2) * 64 + jj + b * NWV + 16 * (cc & 3)] = m[b][e];
+          }
       }
     }
   }
