@@ -559,56 +559,51 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 ? 2 : 1) void k_select(const voi
 
 // ---------------------------------------------------------------------------------------
 // k_csr: row_ptr (exclusive scan of counts) and ascending col_idx from the kept masks.
-// grid = cdiv(rows, 64), 256 threads: workgroup b owns rows [64b, 64b + 64); its offset is
-// the sum of the per-64-row sums before it.  Each wave expands 16 rows: lane L holds word L
-// of a row's mask (all 16 rows' words are loaded up front), and each 64-block chunk of the
-// row is one 64-bit mask from two lanes, whose set bits give every kept block its output slot
-// (coalesced writes).
+// grid = cdiv(rows, 16), 256 threads; wave w owns rows 16 b + 4 w .. + 3, with no workgroup
+// barrier: a row's offset is the sum of the per-64-row sums before its 64-row block plus the
+// counts of the rows before it inside that block (an exclusive scan across the lanes).  Lane L
+// holds word L of a row's mask (the four rows' words are loaded up front), and each 64-block
+// chunk of a row is one 64-bit mask from two lanes, whose set bits give every kept block its
+// output slot (coalesced writes).
 // ---------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_csr(const int32_t *__restrict__ counts,
                                              const uint32_t *__restrict__ bitmask,
                                              const int32_t *__restrict__ bsum, int rows, int nkw, int nkb,
                                              int32_t *__restrict__ row_ptr, int32_t *__restrict__ col_idx) {
-  __shared__ int s_red[4];
-  __shared__ int s_rp[64];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int b = blockIdx.x;
-  const int r0 = b * 64;
-  uint32_t wv[16];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int r0 = blockIdx.x * 16 + 4 * w;   // this wave's first row
+  if (r0 >= rows) return;                    // wave-uniform
+  uint32_t wv[4];
 #pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    const int rk = r0 + 16 * w + k;
+  for (int k = 0; k < 4; ++k) {
+    const int rk = r0 + k;
     wv[k] = (rk < rows && lane < nkw) ? bitmask[(size_t)rk * nkw + lane] : 0u;
   }
+  const int blk = r0 >> 6;
+  const int cl = (64 * blk + lane < rows) ? counts[64 * blk + lane] : 0;
   int part = 0;
-  for (int i = tid; i < b; i += 256) part += bsum[i];
+  for (int i = lane; i < blk; i += 64) part += bsum[i];
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
-  if (lane == 0) s_red[w] = part;
-  __syncthreads();
-  if (w == 0) {
-    const int base = s_red[0] + s_red[1] + s_red[2] + s_red[3];
-    const int row = r0 + lane;
-    const int c = row < rows ? counts[row] : 0;
-    int incl = c;
+  int incl = cl;
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int o = __shfl_up(incl, off);
-      if (lane >= off) incl += o;
-    }
-    const int rp = base + incl - c;
-    s_rp[lane] = rp;
-    if (row < rows) row_ptr[row] = rp;
-    if (row == rows - 1) row_ptr[rows] = rp + c;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
   }
-  __syncthreads();
+  const int excl = incl - cl;   // counts of the block's rows before row 64 blk + lane
   const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   const int nch = (nkb + 63) >> 6;
 #pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    const int rk = r0 + 16 * w + k;
+  for (int k = 0; k < 4; ++k) {
+    const int rk = r0 + k;
     if (rk >= rows) break;
-    int out = s_rp[16 * w + k];
+    int out = part + __shfl(excl, rk - 64 * blk);
+    const int ck = __shfl(cl, rk - 64 * blk);
+    if (lane == 0) {
+      row_ptr[rk] = out;
+      if (rk == rows - 1) row_ptr[rows] = out + ck;
+    }
     for (int c = 0; c < nch; ++c) {
       const unsigned long long mask = (unsigned long long)(uint32_t)__shfl((int)wv[k], 2 * c) |
                                       ((unsigned long long)(uint32_t)__shfl((int)wv[k], 2 * c + 1) << 32);
@@ -720,7 +715,7 @@ int launch_select(const void *q, const double *ksw, int BH, int d, int dtype, in
 
 int launch_csr(const int32_t *counts, const uint32_t *bitmask, const int32_t *bsum, int rows, int nkw, int nkb,
                int32_t *row_ptr, int32_t *col_idx, hipStream_t st) {
-  hipLaunchKernelGGL(k_csr, dim3(cdiv(rows, 64)), dim3(256), 0, st, counts, bitmask, bsum, rows, nkw, nkb, row_ptr,
+  hipLaunchKernelGGL(k_csr, dim3(cdiv(rows, 16)), dim3(256), 0, st, counts, bitmask, bsum, rows, nkw, nkb, row_ptr,
                      col_idx);
   FV_CHECK_LAUNCH();
   return FVATTN_OK;
