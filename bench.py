@@ -113,8 +113,9 @@ def main():
     ap.add_argument("--workload", default="wan14b_n32760")
     ap.add_argument("--p", type=float, default=None)
     ap.add_argument("--schedule", default="identity", choices=["lpt", "identity", "head_lpt", "xcd"])
-    ap.add_argument("--out", default="f32", choices=["f32", "bf16"],
-                    help="output dtype of the attention (f32 = accumulator precision)")
+    ap.add_argument("--out", default="bf16", choices=["f32", "bf16"],
+                    help="output dtype of the attention: bf16 (the layer's output, rounded to nearest even) or "
+                         "f32 (accumulator precision)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip trace/copy-bandwidth extras (profiling runs)")
@@ -230,7 +231,7 @@ def main():
         try:
             pc = json.load(open(prof))
             same = (pc.get("kernel_source_sha") == _attn_source_sha() and pc.get("p") == p
-                    and pc.get("schedule") == args.schedule and pc.get("routing", "topp") == "topp"
+                    and pc.get("schedule") == args.schedule and pc.get("out", "f32") == args.out and pc.get("routing", "topp") == "topp"
                     and args.mode == "topp" and args.k_min == 1 and args.k_max == 0 and args.window == 0
                     and args.sasa_groups == 0)
             if same:
