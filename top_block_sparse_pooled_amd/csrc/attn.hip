@@ -673,6 +673,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_pp(
   __shared__ __attribute__((aligned(1024))) uint8_t V1[2][C::VBYTES];
   __shared__ uint32_t s_bm[G + 1][MAXW];   // kept key blocks of each query block; row G: union
   __shared__ int s_list[MAXW * 32];        // union, ascending: (key block << 4) | keeping query blocks
+  __shared__ int s_wpre[MAXW];             // union blocks before each bitmap word
   __shared__ float s_xm[2][4][64], s_xl[2][4][64];
   __shared__ int s_n, s_tile;
   static_assert(2 * C::KBYTES >= 4 * NH * 16 * 64 * 4, "exchange area");
@@ -796,19 +797,23 @@ __global__ __launch_bounds__(512, 1) void k_attn_pp(
     }
     // kept lists of the unit's query blocks as LDS bitmaps, then their union as a list
     for (int i = tid; i < (G + 1) * MAXW; i += NTH) (&s_bm[0][0])[i] = 0;
-    __syncthreads();
+    // the unit's rows are consecutive CSR rows: their entries form one range, loaded in one
+    // round (row gi of entry e from the row boundaries)
+    int rb[G + 1];
 #pragma unroll
-    for (int gi = 0; gi < G; ++gi) {
-      if (gi < nrow) {
-        const int b0 = row_ptr[r0 + gi], b1 = row_ptr[r0 + gi + 1];
-        for (int e = b0 + tid; e < b1; e += NTH) {
-          const int j = col_idx[e];
-          atomicOr(&s_bm[gi][j >> 5], 1u << (j & 31));
-          atomicOr(&s_bm[G][j >> 5], 1u << (j & 31));
-        }
-      }
+    for (int gi = 0; gi <= G; ++gi) rb[gi] = row_ptr[r0 + min(gi, nrow)];
+    __syncthreads();
+    for (int e = rb[0] + tid; e < rb[G]; e += NTH) {
+      const int j = col_idx[e];
+      int gi = 0;
+#pragma unroll
+      for (int x = 1; x < G; ++x) gi += e >= rb[x];
+      atomicOr(&s_bm[gi][j >> 5], 1u << (j & 31));
+      atomicOr(&s_bm[G][j >> 5], 1u << (j & 31));
     }
     __syncthreads();
+    // union list, ascending: word prefix counts by one wave, then every thread places the
+    // blocks of its own key positions
     if (w == 0) {
       const uint32_t word = lane < nkw ? s_bm[G][lane] : 0u;
       const int pc = __popc(word);
@@ -818,17 +823,18 @@ __global__ __launch_bounds__(512, 1) void k_attn_pp(
         const int ov = __shfl_up(incl, off);
         if (lane >= off) incl += ov;
       }
-      int pos = incl - pc;
-      uint32_t wd = word;
-      while (wd != 0u) {
-        const int bit = __ffs(wd) - 1;
-        wd &= wd - 1u;
+      if (lane < MAXW) s_wpre[lane] = incl - pc;
+      if (lane == 63) s_n = incl;
+    }
+    __syncthreads();
+    for (int j = tid; j < nkw * 32; j += NTH) {
+      const uint32_t word = s_bm[G][j >> 5];
+      if ((word >> (j & 31)) & 1u) {
         int msk = 0;
 #pragma unroll
-        for (int gi = 0; gi < G; ++gi) msk |= (int)((s_bm[gi][lane] >> bit) & 1u) << gi;
-        s_list[pos++] = ((32 * lane + bit) << 4) | msk;
+        for (int gi = 0; gi < G; ++gi) msk |= (int)((s_bm[gi][j >> 5] >> (j & 31)) & 1u) << gi;
+        s_list[s_wpre[j >> 5] + __popc(word & ((1u << (j & 31)) - 1u))] = (j << 4) | msk;
       }
-      if (lane == 63) s_n = incl;
     }
     __syncthreads();
     const int n = s_n;
