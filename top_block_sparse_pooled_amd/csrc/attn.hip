@@ -5,21 +5,23 @@
 // moving the heaviest units first.  On one GPU the balanced units are (head, query-block)
 // tiles handed to persistent workgroups, heaviest first.
 //
-// gfx950 design of the bf16 kernel (k_attn_bf16):
-//  * one workgroup = one query block of BQ rows, BQ/32 waves, each wave owns 32 query rows;
-//  * per kept key block: the K tile [BK][D] and the V^T tile [D][BK] are staged through LDS
-//    (the next block's global loads are issued into registers before the current block is
-//    computed, so HBM/L2 latency overlaps the MFMA work);
-//  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (K from LDS as operand A, Q held in registers as
-//    operand B), so each lane owns one query column: the softmax row statistics need only
-//    one cross-half exchange (v_permlane32_swap) per block;
-//  * online softmax in float32 with exp2 and the 1/sqrt(d)*log2(e) scale folded into one
-//    multiply; P is rounded to bf16 and fed straight from registers as operand B of
-//    O^T += V^T P^T -- the key order inside each 16-key group of V^T is permuted in memory
-//    (bits 2 and 3 of the key index swapped) so that the lane's P registers and its 16-byte
-//    V^T read cover the same keys;
-//  * persistent grid: workgroups pop tiles from a device work list through one atomic
-//    counter, so long rows start first and short rows fill the tail.
+// gfx950 design of the bf16 kernels:
+//  * a work unit is 128 query rows = 128/BQ adjacent query blocks of one head; a persistent
+//    grid of workgroups pops units from a device work list through an atomic ticket, so the
+//    order (identity, heaviest first, ...) is the plan's choice;
+//  * the unit walks the ascending union of its query blocks' kept key blocks; each block's K
+//    and V tiles go into LDS once, straight from global memory (buffer_load ... lds), and every
+//    wave whose query block kept the block uses them;
+//  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (K from LDS as operand A, Q in registers as
+//    operand B), so each lane owns one query column and the softmax row statistics need one
+//    cross-half exchange (v_permlane32_swap) per block;
+//  * online softmax in float32 with exp2 and the 1/sqrt(d)*log2(e) scale folded into one FMA;
+//    P is rounded to bf16 and fed from registers as operand B of O^T += V^T P^T;
+//  * 64-key blocks (k_attn_pp): 8 waves in two groups that split the union and alternate MFMA
+//    and softmax phases; V tiles keep V's layout and the V^T operand comes from transposing
+//    LDS reads;
+//  * 32-key blocks (k_attn_bf16): 4 waves, one pass over the union, V^T tiles from a transposed
+//    copy of V (k_vt) whose key order inside each 16-key group matches the lane's P registers.
 #include <type_traits>
 
 #include "common.h"
@@ -237,8 +239,8 @@ __global__ __launch_bounds__(1024) void k_worklist(const int32_t *__restrict__ r
 }
 
 // ---------------------------------------------------------------------------------------
-// bf16 MFMA attention.  Template: BQ query rows per query block (32/64/128), BK keys per key
-// block (32/64), D head dim (64/128).
+// bf16 MFMA attention for 32-key blocks (k_attn_bf16).  Template: BQ query rows per query
+// block (32/64/128), BK keys per key block, D head dim (64/128).
 //
 // A workgroup is 4 waves = 128 query rows = G = 128/BQ adjacent query blocks of one head (a
 // work unit); each wave owns 32 query rows of one of them.  The workgroup walks the union of
