@@ -6,34 +6,32 @@
 // section "AI视频生成的阿喀琉斯之踵"; pooled scores with 1/sqrt(d): tutorial page, section 5.2.
 //
 // Design (gfx950):
-//  * k_pool      HBM-bound pass over Q or K: each workgroup streams whole blocks with 16-byte
-//                loads, accumulates in float64 (the mean of a block of bf16 values is then
-//                exact up to the final division), and writes the pooled rows in the lane
-//                order the float64 MFMA of k_select consumes (one 512-byte load per operand).
-//  * k_select    one workgroup = 16 query blocks of one head, 4 waves.  Scores
-//                qbar.kbar^T/sqrt(d) come from v_mfma_f64_16x16x4 and stay in registers
-//                (wave w holds key tiles w, w+4, ...).  Softmax numerators e = exp(s - max)
-//                in float64; masses as 2^-52 fixed point so every partial sum is exact and
-//                order independent.  The descending order is never materialised: a radix
-//                select over the float64 bit pattern of e (monotone for e >= 0) splits the
-//                row's key range [e_min, 1] into 256 bins, walks the mass histogram from the
-//                largest bin down, stops at the bin where the cumulative mass crosses p * Z,
-//                and refines that bin the same way until one key remains.  That gives exactly the shortest
-//                prefix of the (e descending, index ascending) order with mass >= p: elements
-//                above the threshold key are all kept, and among keys equal to the threshold
-//                the lowest indices are taken first.
-//  * k_csr       exclusive scan of per-row counts (each workgroup sums the counts before its
-//                range itself, no second pass) and expansion of the kept-bit masks into
-//                ascending column indices.
+//  * k_pool      HBM-bound pass over K (and the exported pooling call): each workgroup streams
+//                whole blocks with 16-byte loads, accumulates in float64 (the mean of a block
+//                of bf16 values is then exact up to the final division), and writes the
+//                pooled rows in the lane order the float64 MFMA of k_select consumes (one
+//                512-byte load per operand).
+//  * k_select    one item = 16 query blocks of one head (4 waves; 8 above 512 key blocks),
+//                persistent.  The item pools its own query blocks into LDS (same summation
+//                order as k_pool), so the raw Q reads overlap other workgroups' work.  Scores
+//                qbar.kbar^T/sqrt(d) come from v_mfma_f64_16x16x4 and stay in registers (wave
+//                w holds key tiles w, w + NWV, ...).  Softmax numerators e = exp(s - max) in
+//                float64; masses as 2^-52 fixed point so every partial sum is exact and order
+//                independent.  The rows then go to LDS and each wave resolves whole rows
+//                alone: the descending order is never materialised; a radix select over the
+//                float64 bit pattern of e (monotone for e >= 0) splits the row's key range
+//                [e_min, 1] into 256 bins (a histogram private to the wave), walks the mass
+//                histogram from the largest bin down, stops at the bin where the cumulative
+//                mass crosses p * Z, and refines that bin the same way until one key remains.
+//                That gives exactly the shortest prefix of the (e descending, index ascending)
+//                order with mass >= p: elements above the threshold key are all kept, and
+//                among keys equal to the threshold the lowest indices are taken first.
+//  * k_csr       exclusive scan of per-row counts (a row's offset is the per-64-row sums
+//                before its block plus a lane scan inside it, no second pass) and expansion
+//                of the kept-bit masks into ascending column indices.
 #include "common.h"
 
 namespace fv {
-
-// Swizzled index of pooled element (block j, dim c) for the f64 MFMA operand layout:
-// lane l of 16x16x4 supplies row (l % 16) and k-index (l / 16).
-__device__ __forceinline__ size_t swz(int bh, int ngroups, int D, int j, int c) {
-  return ((size_t)(bh * ngroups + (j >> 4)) * (D / 4) + (c >> 2)) * 64 + (j & 15) + 16 * (c & 3);
-}
 
 // ---------------------------------------------------------------------------------------
 // k_pool: x [BH][N][D] -> mean of every block of `block` tokens (real tokens only), for one
