@@ -90,3 +90,28 @@ def test_random_shape_parity(label, args, p):
         assert err.max() <= BF16_MAX_ABS and err.mean() <= BF16_MEAN_ABS
     else:
         assert err.max() <= F32_MAX_ABS
+
+
+def test_batch_equals_heads():
+    """B > 1 is more heads: the same 4 heads routed and attended as [2, 2, N, d] and as
+    [1, 4, N, d] give identical CSRs, loads and outputs, and the CSR matches the oracle."""
+    w = workloads.small_case(4, 1700, 128, 64, 64, 950, ("uniform", 0.0, 3.5), "bf16", (2, 25, 34))
+    say("batch B=2 H=2 vs B=1 H=4, N=1700")
+    q, k, v = workloads.make_qkv(w)
+    outs = []
+    for shape in ((1, 4), (2, 2)):
+        qd, kd, vd = (to_dev(x.reshape(*shape, w.N, w.d), "bf16") for x in (q, k, v))
+        csr = fv.route(qd, kd, w.block_q, w.block_k, 0.85)
+        o = fv.sparse_attn(qd, kd, vd, csr)
+        torch.cuda.synchronize()
+        rp = csr.row_ptr.cpu().numpy()
+        outs.append((rp, csr.col_idx[: int(rp[-1])].cpu().numpy(), csr.head_load.cpu().numpy(),
+                     o.reshape(1, 4, w.N, w.d).cpu()))
+    (rp1, ci1, hl1, o1), (rp2, ci2, hl2, o2) = outs
+    np.testing.assert_array_equal(rp1, rp2)
+    np.testing.assert_array_equal(ci1, ci2)
+    np.testing.assert_array_equal(hl1, hl2)
+    assert torch.equal(o1, o2)
+    r = oracle.route(q, k, w.block_q, w.block_k, 0.85)
+    np.testing.assert_array_equal(rp1.astype(np.int64), r["row_ptr"])
+    np.testing.assert_array_equal(ci1.astype(np.int64), r["col_idx"])
