@@ -211,22 +211,27 @@ __global__ __launch_bounds__(256) void k_sasa_mark(const double *__restrict__ im
                                                    const SasaGroup *__restrict__ grp, const int32_t *__restrict__ tiepre,
                                                    int32_t *__restrict__ counts, int32_t *__restrict__ head_load,
                                                    int32_t *__restrict__ bsum) {
-  const int lane = threadIdx.x & 63;
-  const int bh = blockIdx.y, i = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (i >= nqb) return;
-  const size_t row = (size_t)bh * nqb + i;
+  __shared__ int s_add[4];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int bh = blockIdx.y, i = blockIdx.x * 4 + w;
   const SasaGroup G = grp[group_of(bh, R, BH)];
-  if (G.state == 4) return;
-  const unsigned long long need = G.target - G.above;   // ties to take (state 2)
-  unsigned long long rank = G.state == 2 ? (unsigned long long)tiepre[row] : 0ull;
+  if (G.state == 4) return;   // uniform over the workgroup (one head)
   int added = 0;
-  for (int j0 = 0; j0 < nkb; j0 += 64) {
-    const int j = j0 + lane;
-    bool add = false, tie = false;
-    if (j < nkb) {
-      const bool kept = (bitmask[row * nkw + (j >> 5)] >> (j & 31)) & 1u;
-      const unsigned long long key = (unsigned long long)__double_as_longlong(imp[row * nkb + j]);
-      if (!kept) {
+  if (i < nqb) {   // wave-uniform
+    const size_t row = (size_t)bh * nqb + i;
+    const unsigned long long need = G.target - G.above;   // ties to take (state 2)
+    unsigned long long rank = G.state == 2 ? (unsigned long long)tiepre[row] : 0ull;
+    // lane L < nkw holds word L of the row's kept mask; the chunk of key blocks 64c .. 64c+63
+    // is words 2c and 2c + 1
+    uint32_t word = lane < nkw ? bitmask[row * nkw + lane] : 0u;
+    const uint32_t word0 = word;
+    for (int j0 = 0; j0 < nkb; j0 += 64) {
+      const int j = j0 + lane;
+      const uint32_t src = (uint32_t)__shfl((int)word0, j >> 5);
+      const bool kept = (src >> (j & 31)) & 1u;
+      bool add = false, tie = false;
+      if (j < nkb && !kept) {
+        const unsigned long long key = (unsigned long long)__double_as_longlong(imp[row * nkb + j]);
         if (G.state == 3) add = true;
         else if (G.state == 1) add = key >= G.lo;
         else {   // state 2: strictly above the tie key, or a tie within the remaining need
@@ -234,25 +239,34 @@ __global__ __launch_bounds__(256) void k_sasa_mark(const double *__restrict__ im
           add = key > G.lo;
         }
       }
+      if (G.state == 2) {
+        const unsigned long long tb = __ballot(tie);
+        const unsigned long long below = tb & ((1ull << lane) - 1ull);
+        if (tie && rank + (unsigned long long)__popcll(below) < need) add = true;
+        rank += (unsigned long long)__popcll(tb);
+      }
+      const unsigned long long ab = __ballot(add);
+      added += __popcll(ab);
+      if (lane == (j0 >> 5)) word |= (uint32_t)ab;
+      if (lane == (j0 >> 5) + 1) word |= (uint32_t)(ab >> 32);
     }
-    if (G.state == 2) {
-      const unsigned long long tb = __ballot(tie);
-      const unsigned long long below = tb & ((1ull << lane) - 1ull);
-      if (tie && rank + (unsigned long long)__popcll(below) < need) add = true;
-      rank += (unsigned long long)__popcll(tb);
-    }
-    const unsigned long long ab = __ballot(add);
-    added += __popcll(ab);
-    if (lane == 0 && ab != 0ull) {
-      const int w0 = j0 >> 5;
-      if ((uint32_t)ab) bitmask[row * nkw + w0] |= (uint32_t)ab;
-      if ((uint32_t)(ab >> 32) && w0 + 1 < nkw) bitmask[row * nkw + w0 + 1] |= (uint32_t)(ab >> 32);
-    }
+    if (lane < nkw && word != word0) bitmask[row * nkw + lane] = word;
+    if (lane == 0 && added > 0) counts[row] += added;
   }
-  if (lane == 0 && added > 0) {
-    counts[row] += added;
-    atomicAdd(&head_load[bh], added);
-    atomicAdd(&bsum[row >> 6], added);
+  // the workgroup's four rows: one load update for the head, at most two per-64-row sums
+  if (lane == 0) s_add[w] = added;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const size_t row0 = (size_t)bh * nqb + blockIdx.x * 4;
+    int tot = 0, c0 = 0, c1 = 0;
+    for (int r = 0; r < 4; ++r) {
+      tot += s_add[r];
+      if (((row0 + r) >> 6) == (row0 >> 6)) c0 += s_add[r];
+      else c1 += s_add[r];
+    }
+    if (tot > 0) atomicAdd(&head_load[bh], tot);
+    if (c0 > 0) atomicAdd(&bsum[row0 >> 6], c0);
+    if (c1 > 0) atomicAdd(&bsum[(row0 >> 6) + 1], c1);
   }
 }
 
