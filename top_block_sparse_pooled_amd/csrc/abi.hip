@@ -10,6 +10,7 @@ int launch_pool(const void *x, int BH, int N, int d, int dtype, int block, doubl
 int launch_pool_k(const void *k, int BH, int N, int d, int dtype, int block_k, double *ksw, int32_t *zero0, int nzero0,
                   int32_t *zero1, int nzero1, hipStream_t st);
 size_t sasa_group_bytes(int R);
+size_t sasa_hist_bytes(int R);
 int launch_sasa(const double *imp, uint32_t *bitmask, int32_t *counts, int32_t *bsum, int32_t *head_load, int nkw,
                 int nqb, int nkb, int BH, int R, int critical, double alpha, double tau, void *grp_buf,
                 uint32_t *ghist, int32_t *tiecnt, int32_t *tiepre, int32_t *added_out, hipStream_t st);
@@ -104,7 +105,7 @@ SasaWs sasa_ws_layout(const Shape &s, int R, char *base) {
   w.grp = base + off;
   off += align256(fv::sasa_group_bytes(R));
   w.ghist = (uint32_t *)(base + off);
-  off += align256((size_t)R * 256 * sizeof(uint32_t));
+  off += align256(fv::sasa_hist_bytes(R));
   w.tiecnt = (int32_t *)(base + off);
   off += align256((size_t)s.rows * sizeof(int32_t));
   w.tiepre = (int32_t *)(base + off);

@@ -17,7 +17,7 @@
 //  * k_sasa_hist     per pass: histogram of the candidates' keys (float64 bit patterns of P,
 //                    monotone for P >= 0) in each searching group's current range
 //  * k_sasa_resolve  per pass: the bin where the count from the top reaches the budget;
-//                    narrows the range (8 passes resolve any float64 key)
+//                    narrows the range (11-bit digits: 6 passes resolve any key in [0, 1])
 //  * k_sasa_ties     candidates equal to a group's threshold key, per row; k_sasa_tiescan
 //                    turns them into a per-group running rank in row order
 //  * k_sasa_mark     adds the selected blocks to the kept bitmask, counts, loads and sums
@@ -33,6 +33,16 @@ struct SasaGroup {
 };
 
 __device__ __forceinline__ int group_of(int h, int R, int BH) { return (int)(((long long)h * R) / BH); }
+
+// Radix passes over the candidates' keys use 11-bit digits (2048 bins): a key range of the
+// whole [0, 1] (62 bits wide) resolves in at most 6 passes.
+constexpr int kSasaBits = 11, kSasaBins = 1 << kSasaBits;
+constexpr int kSasaPasses = (62 + kSasaBits - 1) / kSasaBits;
+
+__device__ __forceinline__ int sasa_shift(unsigned long long width) {
+  const unsigned long long wm1 = width - 1ull;
+  return wm1 < (unsigned long long)kSasaBins ? 0 : 64 - __clzll((long long)wm1) - kSasaBits;
+}
 
 // One workgroup: group loads, critical path, budgets.
 __global__ __launch_bounds__(1024) void k_sasa_init(const int32_t *__restrict__ head_load, int BH, int R,
@@ -78,8 +88,8 @@ __global__ __launch_bounds__(1024) void k_sasa_init(const int32_t *__restrict__ 
     G.load = L;
     grp[g] = G;
     if (added_out != nullptr) added_out[g] = (int)budget;
-    for (int b = 0; b < 256; ++b) ghist[(size_t)g * 256 + b] = 0;
   }
+  for (size_t b = tid; b < (size_t)R * kSasaBins; b += 1024) ghist[b] = 0;
 }
 
 // grid = (cdiv(nqb, kRowsPerWg), BH), 256 threads: rows [i0, i0 + kRowsPerWg) of head bh.
@@ -88,14 +98,14 @@ constexpr int kRowsPerWg = 8;
 __global__ __launch_bounds__(256) void k_sasa_hist(const double *__restrict__ imp, const uint32_t *__restrict__ bitmask,
                                                    int nkw, int nqb, int nkb, int R, int BH,
                                                    const SasaGroup *__restrict__ grp, uint32_t *__restrict__ ghist) {
-  __shared__ uint32_t h[256];
+  __shared__ uint32_t h[kSasaBins];
   const int bh = blockIdx.y, g = group_of(bh, R, BH);
   const SasaGroup G = grp[g];
   if (G.state != 0) return;   // uniform over the workgroup
   const int tid = threadIdx.x;
-  h[tid] = 0;
+  for (int b = tid; b < kSasaBins; b += 256) h[b] = 0;
   __syncthreads();
-  const int sh = digit_shift(G.width);
+  const int sh = sasa_shift(G.width);
   const int i0 = blockIdx.x * kRowsPerWg, i1 = min(i0 + kRowsPerWg, nqb);
   for (int i = i0; i < i1; ++i) {
     const size_t row = (size_t)bh * nqb + i;
@@ -107,22 +117,26 @@ __global__ __launch_bounds__(256) void k_sasa_hist(const double *__restrict__ im
     }
   }
   __syncthreads();
-  if (h[tid] != 0) atomicAdd(&ghist[(size_t)g * 256 + tid], h[tid]);
+  for (int b = tid; b < kSasaBins; b += 256)
+    if (h[b] != 0) atomicAdd(&ghist[(size_t)g * kSasaBins + b], h[b]);
 }
 
-// One wave per group: find the bin where the count from the top reaches the budget.
+// One wave per group: find the bin where the count from the top reaches the budget (lane l
+// holds bins 32 l .. 32 l + 31).
 __global__ __launch_bounds__(256) void k_sasa_resolve(int R, SasaGroup *__restrict__ grp, uint32_t *__restrict__ ghist) {
+  constexpr int PL = kSasaBins / 64;   // bins per lane
   const int lane = threadIdx.x & 63;
   const int g = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (g >= R) return;
   SasaGroup G = grp[g];
   if (G.state != 0) return;   // uniform over the wave
-  uint32_t c4[4];
+  uint32_t c[PL];
   unsigned long long cs = 0;
+  uint32_t *hg = ghist + (size_t)g * kSasaBins + PL * lane;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    c4[q] = ghist[(size_t)g * 256 + 4 * lane + q];
-    cs += c4[q];
+  for (int q = 0; q < PL; ++q) {
+    c[q] = hg[q];
+    cs += c[q];
   }
   unsigned long long sm = cs;   // inclusive suffix sum over lanes (higher lanes: larger keys)
 #pragma unroll
@@ -131,25 +145,23 @@ __global__ __launch_bounds__(256) void k_sasa_resolve(int R, SasaGroup *__restri
     if (lane + off < 64) sm += o;
   }
   unsigned long long above = sm - cs;
-  const int sh = digit_shift(G.width);
-  int hit = 0;
-  for (int q = 3; q >= 0; --q) {
+  const int sh = sasa_shift(G.width);
+#pragma unroll
+  for (int q = PL - 1; q >= 0; --q) {
     const unsigned long long lo = G.above + above;
-    if (c4[q] > 0 && lo < G.target && G.target <= lo + c4[q]) {
+    if (c[q] > 0 && lo < G.target && G.target <= lo + c[q]) {
       SasaGroup N = G;
       N.above = lo;
-      N.lo = G.lo + ((unsigned long long)(4 * lane + q) << sh);
+      N.lo = G.lo + ((unsigned long long)(PL * lane + q) << sh);
       N.width = 1ull << sh;
-      if (c4[q] == 1) N.state = 1;
+      if (c[q] == 1) N.state = 1;
       else if (sh == 0) N.state = 2;
       grp[g] = N;
-      hit = 1;
     }
-    above += c4[q];
+    above += c[q];
   }
-  (void)hit;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) ghist[(size_t)g * 256 + 4 * lane + q] = 0;   // ready for the next pass
+  for (int q = 0; q < PL; ++q) hg[q] = 0;   // ready for the next pass
 }
 
 // One wave per row: candidates equal to the group's threshold key (state 2).
@@ -271,6 +283,7 @@ __global__ __launch_bounds__(256) void k_sasa_mark(const double *__restrict__ im
 }
 
 size_t sasa_group_bytes(int R) { return (size_t)R * sizeof(SasaGroup); }
+size_t sasa_hist_bytes(int R) { return (size_t)R * kSasaBins * sizeof(uint32_t); }
 
 int launch_sasa(const double *imp, uint32_t *bitmask, int32_t *counts, int32_t *bsum, int32_t *head_load, int nkw,
                 int nqb, int nkb, int BH, int R, int critical, double alpha, double tau, void *grp_buf,
@@ -280,7 +293,7 @@ int launch_sasa(const double *imp, uint32_t *bitmask, int32_t *counts, int32_t *
                      ghist, added_out);
   FV_CHECK_LAUNCH();
   const dim3 gh(cdiv(nqb, kRowsPerWg), BH), gr(cdiv(R, 4)), gw(cdiv(nqb, 4), BH);
-  for (int pass = 0; pass < 8; ++pass) {
+  for (int pass = 0; pass < kSasaPasses; ++pass) {
     hipLaunchKernelGGL(k_sasa_hist, gh, dim3(256), 0, st, imp, bitmask, nkw, nqb, nkb, R, BH, grp, ghist);
     FV_CHECK_LAUNCH();
     hipLaunchKernelGGL(k_sasa_resolve, gr, dim3(256), 0, st, R, grp, ghist);
