@@ -127,6 +127,9 @@ def main():
     ap.add_argument("--sasa-groups", type=int, default=0, help="SASA over this many head groups (0: off)")
     ap.add_argument("--sasa-alpha", type=float, default=0.5, help="SASA augmentation coefficient")
     ap.add_argument("--sasa-tau", type=float, default=0.0, help="SASA trigger threshold")
+    ap.add_argument("--route-every", type=int, default=1,
+                    help="route on every K-th step only and reuse the CSR in between (lazy refresh of the "
+                         "sparse pattern across diffusion steps; 1: route every step)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -165,10 +168,15 @@ def main():
     if args.mode == "topk" and args.topk < 1:
         raise SystemExit("--mode topk needs --topk >= 1")
 
-    def step(ev=None):
+    if args.route_every < 1:
+        raise SystemExit("--route-every needs K >= 1")
+
+    def step(ev=None, do_route=True):
         if ev is not None:
             ev[0].record()
-        if args.sasa_groups > 0:
+        if not do_route:
+            pass   # the CSR of the last refresh is reused; the plan is rebuilt (it may hold a copy of v)
+        elif args.sasa_groups > 0:
             fv.route_sasa(qd, kd, w.block_q, w.block_k, p, groups=args.sasa_groups, alpha=args.sasa_alpha,
                           tau=args.sasa_tau, csr=csr, ws=sws, **variant)
         else:
@@ -190,12 +198,13 @@ def main():
     log(f"[bench] timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    routed = [i % args.route_every == 0 for i in range(args.steps)]
     for i in range(args.steps):
-        step(evs[i])
+        step(evs[i], routed[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = 1e3 * wall / args.steps
-    route_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    route_ms = float(np.mean([e[0].elapsed_time(e[1]) for e, r in zip(evs, routed) if r]))
     plan_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     attn_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
 
@@ -288,7 +297,7 @@ def main():
         config=dict(workload=w.name, B=1, H=w.H, N=w.N, d=w.d, block_q=w.block_q, block_k=w.block_k, p=p,
                     routing=(variant if (args.mode != "topp" or args.k_min != 1 or args.k_max or args.window)
                              else "topp"),
-                    sasa=sasa_info,
+                    sasa=sasa_info, route_every=args.route_every,
                     schedule=args.schedule, out=args.out, nnz=nnz, kept_frac=nnz / (w.rows * w.nkb),
                     executed_tflop=flops / 1e12, nominal_tflop=flops_nominal / 1e12),
         stages_ms=dict(route=route_ms, plan=plan_ms, attn=attn_ms),

@@ -172,6 +172,9 @@ int fvattn_pool(const void *x, int BH, int N, int d, int dtype, int block, doubl
  *   p          in (0, 1]
  *   csr        caller-filled pointers and capacity; shape fields are written
  *   ws         device workspace of at least fvattn_route_ws_bytes(...) bytes
+ * The CSR is plain caller memory and may be applied to later q, k, v of the same shape: the
+ * Baidu Cloud video-engine tutorial (step 2, dynamic sparse attention) refreshes the sparse
+ * pattern only every few diffusion steps.  Attention over a given CSR is exact for any inputs.
  */
 int fvattn_route(const void *q, const void *k, int B, int H, int N, int d, int dtype,
                  int block_q, int block_k, double p, fvattn_csr *csr, void *ws,

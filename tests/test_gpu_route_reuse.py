@@ -1,0 +1,77 @@
+"""GPU: one routing reused over several steps (lazy refresh of the sparse pattern every few
+diffusion steps, Baidu Cloud video-engine tutorial, "第二步：采用动态稀疏注意力机制降低计算量").
+
+The CSR routed on the first step's q, k is applied to later steps' q, k, v.  Attention over a
+given kept set is exact whatever inputs it meets, so every step's output must match the
+oracle's sparse attention of that step's inputs over the first step's oracle CSR.  With
+64-token key blocks the plan (a work list) is built once and rerun; with 32-token key blocks
+the plan also holds a transposed copy of v, so it is rebuilt whenever v changes."""
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle
+import workloads
+from _parity import BF16_MAX_ABS, BF16_MEAN_ABS, record
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("no GPU", allow_module_level=True)
+
+import top_block_sparse_pooled_amd as fv
+
+DEV = torch.device("cuda:0")
+
+
+def say(msg):
+    print(f"[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16).to(DEV).contiguous()
+
+
+CASES = [
+    # (label, (H, N, d, block_q, block_k, alpha range, grid), p)
+    ("bk64_h2_n2100_d128", (2, 2100, 128, 64, 64, ("uniform", 0.0, 3.5), (3, 20, 35)), 0.9),
+    ("bk32_h2_n1900_d64", (2, 1900, 64, 64, 32, ("uniform", 0.5, 3.0), (5, 19, 20)), 0.85),
+]
+
+
+@pytest.mark.parametrize("label,shape,p", CASES, ids=[c[0] for c in CASES])
+def test_route_reused_across_steps(label, shape, p):
+    H, N, d, bq, bk, alpha, grid = shape
+    # three "steps": seeds 0, 1, 0 again (the third must reproduce the first bitwise)
+    steps = [workloads.small_case(H, N, d, bq, bk, seed, alpha, "bf16", grid) for seed in (960, 961, 960)]
+    ins = [workloads.make_qkv(w) for w in steps]
+    w0 = steps[0]
+    say(f"route reuse {label}: route on step 0, attend steps 0..2")
+    q0, k0, _ = ins[0]
+    ref_csr = oracle.route(q0, k0, bq, bk, p)
+    csr = fv.route(to_dev(q0), to_dev(k0), bq, bk, p)
+    torch.cuda.synchronize()
+    rp = csr.row_ptr.cpu().numpy().astype(np.int64)
+    np.testing.assert_array_equal(rp, ref_csr["row_ptr"])
+    np.testing.assert_array_equal(csr.col_idx[: int(rp[-1])].cpu().numpy().astype(np.int64), ref_csr["col_idx"])
+
+    ws = fv.attn_ws(to_dev(q0), csr)
+    outs = []
+    for s, (q, k, v) in enumerate(ins):
+        qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+        if s == 0 or bk == 32:
+            fv.attn_plan(vd, csr, ws, "lpt")
+        o = fv.attn_run(qd, kd, vd, csr, ws, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        outs.append(o.cpu())
+        ref = oracle.sparse_attention(q, k, v, ref_csr["row_ptr"], ref_csr["col_idx"], bq, bk)
+        err = np.abs(o.cpu().numpy() - ref)
+        record(f"route_reuse/{label}/step{s}", dict(rows=w0.rows, max_abs=float(err.max()),
+                                                     mean_abs=float(err.mean())))
+        assert err.max() <= BF16_MAX_ABS and err.mean() <= BF16_MEAN_ABS, (s, float(err.max()))
+    assert torch.equal(outs[0], outs[2])
+    assert not torch.equal(outs[0], outs[1])
