@@ -312,11 +312,9 @@ def main():
 
 
 def attn_kernel_name(w):
-    """The bf16 attention kernel the library runs for this workload (64-key blocks: two
-    wave groups per unit; 32-key blocks: one group)."""
-    if w.dtype != "bf16":
-        return "k_attn_f32"
-    return "k_attn_pp" if w.block_k == 64 else "k_attn_bf16"
+    """The attention kernel the library runs for this workload (bf16: two wave groups per
+    unit over 64-key tiles of one or two key blocks)."""
+    return "k_attn_pp" if w.dtype == "bf16" else "k_attn_f32"
 
 
 def _attn_source_sha():

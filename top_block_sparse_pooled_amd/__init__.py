@@ -337,7 +337,7 @@ def attn_ws(q, csr: Csr):
 
 
 def attn_plan(v, csr: Csr, ws, schedule: str = "lpt"):
-    """Work list (+ transposed v for bf16) into ws; see fvattn_attn_plan."""
+    """Work list of the CSR rows into ws (v supplies the shape only); see fvattn_attn_plan."""
     _check_qkv(v)
     B, H, N, d = v.shape
     c = csr.c()

@@ -19,12 +19,11 @@ int launch_select(const void *q, const double *ksw, int BH, int d, int dtype, in
                   int k_min, int k_max, int window, int bq, int bk, int N, double *imp, hipStream_t st);
 int launch_csr(const int32_t *counts, const uint32_t *bitmask, const int32_t *bsum, int rows, int nkw, int nkb,
                int32_t *row_ptr, int32_t *col_idx, hipStream_t st);
-int launch_vt(const void *v, void *vt, int BH, int N, int D, int NKP, hipStream_t st);
 int launch_worklist(const int32_t *row_ptr, int rows, int nqb, int nkb, int G, int sched, int32_t *wl,
                     int32_t *counter, hipStream_t st);
-int launch_attn_bf16(const void *q, const void *k, const void *v, const void *vt, void *o, int out_f32,
+int launch_attn_bf16(const void *q, const void *k, const void *v, void *o, int out_f32,
                      const int32_t *row_ptr,
-                     const int32_t *col_idx, const int32_t *wl, int32_t *counter, int rows, int nqb, int N, int NKP,
+                     const int32_t *col_idx, const int32_t *wl, int32_t *counter, int rows, int nqb, int N,
                      int D, int BQ, int BK, int grid, uint64_t *trace, hipStream_t st);
 int launch_attn_f32(const void *q, const void *k, const void *v, void *o, const int32_t *row_ptr,
                     const int32_t *col_idx, const int32_t *wl, int rows, int nqb, int N, int D, int BQ, int BK,
@@ -116,8 +115,6 @@ SasaWs sasa_ws_layout(const Shape &s, int R, char *base) {
 
 struct AttnWs {
   int32_t *worklist, *counter;
-  uint16_t *vt;
-  int nkp;
   size_t bytes;
 };
 
@@ -128,10 +125,7 @@ AttnWs attn_ws_layout(const Shape &s, int dtype, char *base) {
   off += align256((size_t)s.rows * sizeof(int32_t));
   w.counter = (int32_t *)(base + off);
   off += 256;
-  w.nkp = (s.N + 63) / 64 * 64;
-  // transposed V: only the 32-key-block bf16 kernel reads it
-  w.vt = (uint16_t *)(base + off);
-  if (dtype == FVATTN_BF16 && s.bk == 32) off += align256((size_t)s.BH * s.d * w.nkp * sizeof(uint16_t));
+  (void)dtype;
   w.bytes = off;
   return w;
 }
@@ -337,9 +331,8 @@ int do_plan(const void *v, const Shape &s, int dtype, const fvattn_csr *csr, int
             hipStream_t st) {
   // bf16 attention consumes units of 128 query rows (128 / block_q query blocks); fp32: rows
   const int G = dtype == FVATTN_BF16 ? 128 / csr->block_q : 1;
-  int rc = fv::launch_worklist(csr->row_ptr, s.rows, s.nqb, s.nkb, G, sched, w.worklist, w.counter, st);
-  if (rc != FVATTN_OK || dtype == FVATTN_F32 || csr->block_k != 32) return rc;
-  return fv::launch_vt(v, w.vt, s.BH, s.N, s.d, w.nkp, st);
+  (void)v;
+  return fv::launch_worklist(csr->row_ptr, s.rows, s.nqb, s.nkb, G, sched, w.worklist, w.counter, st);
 }
 
 int do_run(const void *q, const void *k, const void *v, void *o, const Shape &s, int dtype, int out_dt,
@@ -347,8 +340,8 @@ int do_run(const void *q, const void *k, const void *v, void *o, const Shape &s,
   if (dtype == FVATTN_F32)
     return fv::launch_attn_f32(q, k, v, o, csr->row_ptr, csr->col_idx, w.worklist, s.rows, s.nqb, s.N, s.d,
                                csr->block_q, csr->block_k, trace, st);
-  return fv::launch_attn_bf16(q, k, v, w.vt, o, out_dt == FVATTN_F32, csr->row_ptr, csr->col_idx, w.worklist,
-                              w.counter, s.rows, s.nqb, s.N, w.nkp, s.d, csr->block_q, csr->block_k, grid, trace, st);
+  return fv::launch_attn_bf16(q, k, v, o, out_dt == FVATTN_F32, csr->row_ptr, csr->col_idx, w.worklist,
+                              w.counter, s.rows, s.nqb, s.N, s.d, csr->block_q, csr->block_k, grid, trace, st);
 }
 }  // namespace
 

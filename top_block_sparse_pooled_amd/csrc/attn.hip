@@ -17,58 +17,14 @@
 //    cross-half exchange (v_permlane32_swap) per block;
 //  * online softmax in float32 with exp2 and the 1/sqrt(d)*log2(e) scale folded into one FMA;
 //    P is rounded to bf16 and fed from registers as operand B of O^T += V^T P^T;
-//  * 64-key blocks (k_attn_pp): 8 waves in two groups that split the union and alternate MFMA
-//    and softmax phases; V tiles keep V's layout and the V^T operand comes from transposing
-//    LDS reads;
-//  * 32-key blocks (k_attn_bf16): 4 waves, one pass over the union, V^T tiles from a transposed
-//    copy of V (k_vt) whose key order inside each 16-key group matches the lane's P registers.
+//  * k_attn_pp: 8 waves in two groups that split the union into 64-key tiles (one 64-token
+//    block or two 32-token blocks) and alternate MFMA and softmax phases; V tiles keep V's
+//    layout and the V^T operand comes from transposing LDS reads.
 #include <type_traits>
 
 #include "common.h"
 
 namespace fv {
-
-// ---------------------------------------------------------------------------------------
-// k_vt: V [BH][N][D] bf16 -> V^T [BH][D][NKP] bf16, zero for keys >= N, keys permuted
-// inside each 16-key group: key 16t + 8c + 4h + b is stored at 16t + 8h + 4c + b.
-// grid = (NKP/64, D/64, BH), 256 threads.
-// ---------------------------------------------------------------------------------------
-__device__ __forceinline__ int vperm(int key) {
-  return (key & ~15) | ((key & 4) << 1) | ((key & 8) >> 1) | (key & 3);
-}
-
-__global__ __launch_bounds__(256) void k_vt(const uint16_t *__restrict__ v, uint16_t *__restrict__ vt, int N,
-                                            int D, int NKP) {
-  __shared__ uint16_t tile[64][64 + 2];
-  const int tid = threadIdx.x;
-  const int key0 = blockIdx.x * 64, d0 = blockIdx.y * 64, bh = blockIdx.z;
-  const uint16_t *vh = v + (size_t)bh * N * D;
-  // read 64 keys x 64 dims: 512 chunks of 8 dims
-  for (int c = tid; c < 512; c += 256) {
-    const int r = c >> 3, dc = (c & 7) * 8;
-    const int key = key0 + r;
-    u32x4 val = {0u, 0u, 0u, 0u};
-    if (key < N) val = *reinterpret_cast<const u32x4 *>(vh + (size_t)key * D + d0 + dc);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      tile[r][dc + 2 * i] = (uint16_t)(val[i] & 0xffffu);
-      tile[r][dc + 2 * i + 1] = (uint16_t)(val[i] >> 16);
-    }
-  }
-  __syncthreads();
-  // write 64 dims x 64 keys: 512 chunks of 8 (permuted) key positions
-  uint16_t *vth = vt + (size_t)bh * D * NKP;
-  for (int c = tid; c < 512; c += 256) {
-    const int dd = c >> 3, pc = (c & 7) * 8;
-    uint32_t wv[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int k0 = vperm(pc + 2 * i), k1 = vperm(pc + 2 * i + 1);  // physical -> logical
-      wv[i] = (uint32_t)tile[k0][dd] | ((uint32_t)tile[k1][dd] << 16);
-    }
-    *reinterpret_cast<u32x4 *>(vth + (size_t)(d0 + dd) * NKP + key0 + pc) = u32x4{wv[0], wv[1], wv[2], wv[3]};
-  }
-}
 
 // ---------------------------------------------------------------------------------------
 // k_worklist: permutation of the work units in the requested order.  A unit is G consecutive
@@ -239,44 +195,29 @@ __global__ __launch_bounds__(1024) void k_worklist(const int32_t *__restrict__ r
 }
 
 // ---------------------------------------------------------------------------------------
-// bf16 MFMA attention for 32-key blocks (k_attn_bf16).  Template: BQ query rows per query
-// block (32/64/128), BK keys per key block, D head dim (64/128).
-//
-// A workgroup is 4 waves = 128 query rows = G = 128/BQ adjacent query blocks of one head (a
-// work unit); each wave owns 32 query rows of one of them.  The workgroup walks the union of
-// the G kept-block lists in ascending key order; each key block's K and V^T tiles are loaded
-// once into LDS and used by every wave whose query block kept it (adjacent query blocks of a
-// video layer keep largely the same blocks), the other waves skip it.
-//
-// LDS holds two K tiles [BK][D] and two V^T tiles [D][BK] filled straight from global memory
-// by buffer_load ... lds (no staging registers; per-head buffer resources make rows past N
+// Geometry of a K or V tile of BK keys x D dims in LDS, loaded by NW waves as 1 KB pieces
+// straight from global memory (buffer_load ... lds; per-head buffer resources make rows past N
 // read as zero).  Rows are runs of 16-byte chunks in XOR-swizzled order (rows that share a
 // 256-byte bank line get different XOR keys) so the 16-byte operand reads of 16 consecutive
-// rows hit distinct banks.  Tiles are double buffered: the next block's loads are issued
-// right after the one barrier per block and have a whole block of compute to land.
+// rows hit distinct banks.
 // ---------------------------------------------------------------------------------------
 template <int BK, int D>
 struct AttnCfg {
-  static constexpr int NW = 4;             // waves per workgroup
+  static constexpr int NW = 4;             // waves loading a tile (one wave group)
   static constexpr int NT = NW * 64;
   static constexpr int KROW = D * 2;       // bytes per K tile row (one key)
   static constexpr int KCR = D / 8;        // 16-byte chunks per K row
-  static constexpr int VROW = BK * 2;      // bytes per V^T tile row (one dim)
-  static constexpr int VCR = BK / 8;       // chunks per V^T row
   static constexpr int KBYTES = BK * D * 2;
   static constexpr int VBYTES = D * BK * 2;
   static constexpr int KI = KBYTES / 1024 / NW;  // 1 KB direct-to-LDS loads per wave
   static constexpr int VI = VBYTES / 1024 / NW;
   static constexpr int KRP = KROW >= 256 ? 1 : 256 / KROW;   // rows sharing one 256-byte bank line
-  static constexpr int VRP = VROW >= 256 ? 1 : 256 / VROW;
   static constexpr int KRPI = 1024 / KROW; // rows per 1 KB load
-  static constexpr int VRPI = 1024 / VROW;
   static constexpr int KPER = (KCR * KRP) / KRPI > 0 ? (KCR * KRP) / KRPI : 1;  // loads before the
-  static constexpr int VPER = (VCR * VRP) / VRPI > 0 ? (VCR * VRP) / VRPI : 1;  // swizzle repeats
-  static_assert(KPER * KRPI == KRP * KCR && VPER * VRPI == VRP * VCR, "swizzle period");
+                                                                                // swizzle repeats
+  static_assert(KPER * KRPI == KRP * KCR, "swizzle period");
   static constexpr bool KTAB = (KI % KPER) == 0;  // load i of every wave has swizzle phase i % KPER
-  static constexpr bool VTAB = (VI % VPER) == 0;
-  static constexpr int NKT = BK / 32;      // 32-key tiles per block
+  static constexpr int NKT = BK / 32;      // 32-key MFMA tiles per tile
   static constexpr int NS = D / 16;        // k-steps of S^T = K Q^T
   static constexpr int NM = D / 32;        // 32-dim tiles of O^T
   static_assert(KBYTES % (1024 * NW) == 0 && VBYTES % (1024 * NW) == 0, "tile/wave mismatch");
@@ -291,13 +232,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, uin
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// 16 bytes per lane from the buffer straight into LDS at lds_dst (wave-uniform) + 16 * lane.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void *lds_dst) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_ptr)lds_dst, 16, voff, soff, 0, 0);
-}
-
-// The same with an instruction offset OFF, which the hardware adds to both the buffer address
-// and the LDS address: consecutive 1 KB pieces of a tile then share one LDS base (M0).
+// 16 bytes per lane from the buffer straight into LDS at lds_dst (wave-uniform) + 16 * lane,
+// with an instruction offset OFF, which the hardware adds to both the buffer address and the
+// LDS address: consecutive 1 KB pieces of a tile then share one LDS base (M0).
 template <int OFF>
 __device__ __forceinline__ void dma16_at(__amdgpu_buffer_rsrc_t r, uint32_t voff, void *lds_dst) {
   static_assert(OFF >= 0 && OFF < 4096, "12-bit instruction offset");
@@ -316,326 +253,15 @@ __device__ __forceinline__ uint64_t hw_id_word() {
   return ((uint64_t)xcc << 32) | hw;
 }
 
-template <int BQ, int BK, int D>
-__global__ __launch_bounds__(256, 2) void k_attn_bf16(
-    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ vt,
-    void *__restrict__ o, int out_f32, const int32_t *__restrict__ row_ptr, const int32_t *__restrict__ col_idx,
-    const int32_t *__restrict__ worklist, int32_t *__restrict__ counter, int units, int ngroups, int nqb, int N,
-    int NKP, float sl2, uint64_t *__restrict__ trace) {
-  using C = AttnCfg<BK, D>;
-  constexpr int G = 128 / BQ;     // query blocks per unit
-  constexpr int WPQ = BQ / 32;    // waves per query block
-  constexpr int NONE = 0x7fffffff;
-  constexpr int MAXW = 40;         // kept-block bitmap words (1280 key blocks)
-  // Two tile buffers per operand, as four separate LDS objects: the main loop is unrolled so
-  // that each half names its buffers statically, which lets the compiler see that the
-  // direct-to-LDS loads into one buffer never alias reads of the other (a single indexed
-  // array would make it wait for the prefetch before every read).
-  __shared__ __attribute__((aligned(1024))) uint8_t Ks0[C::KBYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t Ks1[C::KBYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t Vs0[C::VBYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t Vs1[C::VBYTES];
-  __shared__ uint32_t s_bm[G + 1][MAXW];   // kept key blocks of each query block; row G: union
-  __shared__ int s_tile;
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, kept in an SGPR
-  const int wq = w / WPQ, wr = w % WPQ;                     // query block of the unit, 32-row slice
-  const int nkw = (N + BK * 32 - 1) / (BK * 32);             // bitmap words in use
-  const int l32 = lane & 31, h = lane >> 5;
-
-  // Tile loads: load i of wave w fills LDS bytes [(w*KI + i) KB, +1 KB) of a tile; lane L writes
-  // the 16 bytes at +16 L, i.e. tile row (w*KI + i)*KRPI + L/(row chunks), position
-  // L%(row chunks), and fetches the chunk whose swizzled position that is.  The swizzle repeats
-  // every KPER (VPER) loads, so a handful of per-lane offsets cover all loads.
-  const int k_r0 = lane / C::KCR, k_pos = lane % C::KCR;
-  const int v_r0 = lane / C::VCR, v_pos = lane % C::VCR;
-  uint32_t k_vo[C::KPER], v_vo[C::VPER];
-#pragma unroll
-  for (int j = 0; j < C::KPER; ++j) {
-    const int r = j * C::KRPI + k_r0;
-    k_vo[j] = (uint32_t)(k_r0 * C::KROW + swz_pos(k_pos, r, C::KROW, C::KCR) * 16);
-  }
-#pragma unroll
-  for (int j = 0; j < C::VPER; ++j) {
-    const int r = j * C::VRPI + v_r0;
-    v_vo[j] = (uint32_t)(v_r0 * NKP * 2 + swz_pos(v_pos, r, C::VROW, C::VCR) * 16);
-  }
-
-  const bool per_xcd = counter[2] != 0;
-  const int xcc = (int)(__builtin_amdgcn_s_getreg((31 << 11) | 20) & 7);   // XCC_ID
-  for (;;) {
-    if (tid == 0) {
-      int tk = units;
-      if (!per_xcd) {
-        tk = atomicAdd(&counter[0], 1);
-      } else {
-        for (int qq = 0; qq < 8; ++qq) {     // own XCD's range first, then the others'
-          const int x = (xcc + qq) & 7;
-          const int c = atomicAdd(&counter[8 + x], 1);
-          if (c < counter[17 + x]) {
-            tk = c;
-            break;
-          }
-        }
-      }
-      s_tile = tk;
-    }
-    __syncthreads();
-    const int t = s_tile;
-    __syncthreads();
-    if (t >= units) break;
-    uint64_t t_start = 0;
-    if (trace != nullptr) t_start = __builtin_amdgcn_s_memrealtime();
-
-    const int u = worklist[t];
-    const int bh = u / ngroups, g = u - bh * ngroups;
-    const int r0 = bh * nqb + g * G;                // first CSR row of the unit
-    const int nrow = min(G, nqb - g * G);           // query blocks present in the unit
-    const uint16_t *kh = k + (size_t)bh * N * D;
-    const uint16_t *vth = vt + (size_t)bh * D * NKP;
-    const __amdgpu_buffer_rsrc_t krs = buf_rsrc(kh, (uint32_t)N * D * 2);
-    const __amdgpu_buffer_rsrc_t vrs = buf_rsrc(vth, (uint32_t)D * NKP * 2);
-    auto load_k = [&](int jb, uint8_t *kbuf) {
-      const uint32_t sbase = (uint32_t)jb * BK * D * 2 + (uint32_t)w * C::KI * C::KRPI * C::KROW;
-      uint8_t *dst = kbuf + w * C::KI * 1024;
-#pragma unroll
-      for (int i = 0; i < C::KI; ++i) {
-        uint32_t vo;
-        if constexpr (C::KTAB) {
-          vo = k_vo[i % C::KPER];
-        } else {
-          const int gi = w * C::KI + i;
-          vo = (uint32_t)(k_r0 * C::KROW + swz_pos(k_pos, gi * C::KRPI + k_r0, C::KROW, C::KCR) * 16);
-        }
-        dma16(krs, vo + sbase + (uint32_t)i * C::KRPI * C::KROW, 0, dst + i * 1024);
-      }
-    };
-    auto load_v = [&](int jb, uint8_t *vbuf) {
-      const uint32_t sbase = (uint32_t)jb * BK * 2 + (uint32_t)w * C::VI * C::VRPI * NKP * 2;
-      uint8_t *dst = vbuf + w * C::VI * 1024;
-#pragma unroll
-      for (int i = 0; i < C::VI; ++i) {
-        uint32_t vo;
-        if constexpr (C::VTAB) {
-          vo = v_vo[i % C::VPER];
-        } else {
-          const int gi = w * C::VI + i;
-          vo = (uint32_t)(v_r0 * NKP * 2 + swz_pos(v_pos, gi * C::VRPI + v_r0, C::VROW, C::VCR) * 16);
-        }
-        dma16(vrs, vo + sbase + (uint32_t)i * C::VRPI * NKP * 2, 0, dst + i * 1024);
-      }
-    };
-
-    // the unit's G kept lists as LDS bitmaps (one pass over col_idx per unit); the walk over
-    // their union is then a bit scan, and "does my query block keep it" a bit test
-    for (int i = tid; i < (G + 1) * MAXW; i += C::NT) (&s_bm[0][0])[i] = 0;
-    __syncthreads();
-#pragma unroll
-    for (int gi = 0; gi < G; ++gi) {
-      if (gi < nrow) {
-        const int b0 = row_ptr[r0 + gi], b1 = row_ptr[r0 + gi + 1];
-        for (int e = b0 + tid; e < b1; e += C::NT) {
-          const int j = col_idx[e];
-          atomicOr(&s_bm[gi][j >> 5], 1u << (j & 31));
-          atomicOr(&s_bm[G][j >> 5], 1u << (j & 31));
-        }
-      }
-    }
-    __syncthreads();
-    int uw = 0;                                   // union word index (uniform)
-    uint32_t ubits = (uint32_t)__builtin_amdgcn_readfirstlane(s_bm[G][0]);
-    auto advance = [&](int &jb, int &mask) {
-      while (ubits == 0u && uw + 1 < nkw) {
-        ++uw;
-        ubits = (uint32_t)__builtin_amdgcn_readfirstlane(s_bm[G][uw]);
-      }
-      if (ubits == 0u) {
-        jb = NONE;
-        mask = 0;
-        return;
-      }
-      jb = 32 * uw + (__ffs(ubits) - 1);
-      ubits &= ubits - 1u;
-      mask = 0;
-#pragma unroll
-      for (int gi = 0; gi < G; ++gi) mask |= (int)((s_bm[gi][uw] >> (jb & 31)) & 1u) << gi;
-      mask = __builtin_amdgcn_readfirstlane(mask);
-    };
-    int cur_j, cur_m, nxt_j, nxt_m;
-    advance(cur_j, cur_m);
-    advance(nxt_j, nxt_m);
-    if (cur_j != NONE) {
-      load_k(cur_j, Ks0);
-      load_v(cur_j, Vs0);
-    }
-
-    // this wave's query rows
-    const int qi = g * G + wq;
-    const int qrow = qi * BQ + 32 * wr + l32;
-    const bool qlive = qi < nqb && qrow < N;
-    bf16x8 qf[C::NS];
-    {
-      const uint16_t *qp = q + ((size_t)bh * N + (qlive ? qrow : 0)) * D + 8 * h;
-#pragma unroll
-      for (int s = 0; s < C::NS; ++s) {
-        u32x4 raw = {0u, 0u, 0u, 0u};
-        if (qlive) raw = *reinterpret_cast<const u32x4 *>(qp + 16 * s);
-        qf[s] = __builtin_bit_cast(bf16x8, raw);
-      }
-    }
-    f16v oacc[C::NM];
-#pragma unroll
-    for (int m = 0; m < C::NM; ++m)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[m][i] = 0.f;
-    float m_run = -INFINITY, l_run = 0.f;   // running row maximum (log2 units) and row sum
-
-    // one key block: tiles of cur_j are in (kb, vb); the next block's are loaded into (kn, vn)
-    auto step = [&](const uint8_t *kb, const uint8_t *vb, uint8_t *kn, uint8_t *vn) {
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();                 // tiles of cur_j landed; (kn, vn) no longer read
-      if (nxt_j != NONE) {
-        load_k(nxt_j, kn);
-        load_v(nxt_j, vn);
-      }
-      if ((cur_m >> wq) & 1) {         // wave-uniform: this wave's query block kept cur_j
-        // S^T tiles: 32 keys x 32 queries each
-        f16v sacc[C::NKT];
-#pragma unroll
-        for (int kt = 0; kt < C::NKT; ++kt) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) sacc[kt][i] = 0.f;
-#pragma unroll
-          for (int s = 0; s < C::NS; ++s) {
-            const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(
-                kb + (32 * kt + l32) * C::KROW + swz_pos(2 * s + h, l32, C::KROW, C::KCR) * 16);
-            sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[s], sacc[kt], 0, 0, 0);
-          }
-        }
-        // online softmax (lane: query qrow; keys 32kt + 8(v/4) + 4h + v%4 of the block)
-        const int kbase = cur_j * BK;
-        if (kbase + BK > N) {          // ragged last block: mask keys >= N
-          const int lim = N - kbase - 4 * h;
-#pragma unroll
-          for (int kt = 0; kt < C::NKT; ++kt)
-#pragma unroll
-            for (int v = 0; v < 16; ++v)
-              if (32 * kt + 8 * (v >> 2) + (v & 3) >= lim) sacc[kt][v] = -INFINITY;
-        }
-        float mloc = sacc[0][0];
-#pragma unroll
-        for (int kt = 0; kt < C::NKT; ++kt)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) mloc = fmaxf(mloc, sacc[kt][v]);
-        {
-          auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mloc), __float_as_uint(mloc), false, false);
-          mloc = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-        }
-        const float mb = mloc * sl2;
-        // rescale only when some row's maximum grew (wave-uniform branch); the largest
-        // weight of a row then stays exactly 1, so its bf16 copy carries no rounding error
-        if (__any(mb > m_run)) {
-          const float m_new = fmaxf(m_run, mb);
-          const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-          m_run = m_new;
-          l_run *= alpha;
-#pragma unroll
-          for (int m = 0; m < C::NM; ++m)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) oacc[m][i] *= alpha;
-        }
-        const float nm = -m_run;
-        float psum = 0.f;
-        bf16x8 pf[C::NKT][2];
-#pragma unroll
-        for (int kt = 0; kt < C::NKT; ++kt)
-#pragma unroll
-          for (int t2 = 0; t2 < 2; ++t2) {
-            bf16x8 pv;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-              const float pe = __builtin_amdgcn_exp2f(fmaf(sacc[kt][8 * t2 + i], sl2, nm));
-              psum += pe;
-              pv[i] = (__bf16)pe;
-            }
-            pf[kt][t2] = pv;
-          }
-        l_run += psum;
-        // O^T += V^T P^T
-#pragma unroll
-        for (int m = 0; m < C::NM; ++m)
-#pragma unroll
-          for (int kt = 0; kt < C::NKT; ++kt)
-#pragma unroll
-            for (int t2 = 0; t2 < 2; ++t2) {
-              const bf16x8 va = *reinterpret_cast<const bf16x8 *>(
-                  vb + (32 * m + l32) * C::VROW + swz_pos(4 * kt + 2 * t2 + h, l32, C::VROW, C::VCR) * 16);
-              oacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[kt][t2], oacc[m], 0, 0, 0);
-            }
-      }
-      cur_j = nxt_j;
-      cur_m = nxt_m;
-      advance(nxt_j, nxt_m);
-    };
-    while (cur_j != NONE) {
-      step(Ks0, Vs0, Ks1, Vs1);
-      if (cur_j == NONE) break;
-      step(Ks1, Vs1, Ks0, Vs0);
-    }
-
-    // finalise: l over both halves, O / l, store (lane: query qrow, dims 32m + 8a + 4h + b)
-    {
-      auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
-      const float ltot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-      const float inv = 1.f / ltot;
-      if (qlive && out_f32) {
-        float *op = (float *)o + ((size_t)bh * N + qrow) * D + 4 * h;
-#pragma unroll
-        for (int m = 0; m < C::NM; ++m)
-#pragma unroll
-          for (int a = 0; a < 4; ++a)
-            *reinterpret_cast<f4 *>(op + 32 * m + 8 * a) =
-                f4{oacc[m][4 * a] * inv, oacc[m][4 * a + 1] * inv, oacc[m][4 * a + 2] * inv, oacc[m][4 * a + 3] * inv};
-      } else if (qlive) {
-        uint16_t *op = (uint16_t *)o + ((size_t)bh * N + qrow) * D + 4 * h;
-#pragma unroll
-        for (int m = 0; m < C::NM; ++m)
-#pragma unroll
-          for (int a = 0; a < 4; ++a) {
-            const uint32_t w0 = pack_bf16(oacc[m][4 * a] * inv, oacc[m][4 * a + 1] * inv);
-            const uint32_t w1 = pack_bf16(oacc[m][4 * a + 2] * inv, oacc[m][4 * a + 3] * inv);
-            *reinterpret_cast<u32x2 *>(op + 32 * m + 8 * a) = u32x2{w0, w1};
-          }
-      }
-    }
-    if (trace != nullptr && tid == 0) {
-      const uint64_t t_end = __builtin_amdgcn_s_memrealtime();
-      trace[4 * (size_t)t + 0] = hw_id_word();
-      trace[4 * (size_t)t + 1] = t_start;
-      trace[4 * (size_t)t + 2] = t_end;
-      trace[4 * (size_t)t + 3] = (uint64_t)u;
-    }
-  }
-  // The last workgroup to leave has seen every other workgroup's final ticket: restore the
-  // ticket counters and the exit count so the same plan can be run again.
-  if (tid == 0) {
-    __threadfence();
-    if (atomicAdd(&counter[1], 1) == (int)gridDim.x - 1) {
-      atomicExch(&counter[0], 0);
-      for (int x = 0; x < 8; ++x) atomicExch(&counter[8 + x], counter[16 + x]);
-      atomicExch(&counter[1], 0);
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------------------
-// bf16 MFMA attention for 64-key blocks, two wave groups per unit (k_attn_pp).
+// bf16 MFMA attention, two wave groups per unit (k_attn_pp).
 //
 // A workgroup is 8 waves in two groups of 4.  Both groups cover the same 128 query rows (one
-// work unit, as in k_attn_bf16) and split the unit's ascending union of kept key blocks:
-// group g takes entries g, g+2, g+4, ... with its own online-softmax state, and the two
-// partial results (row maximum, row sum, O) are merged through LDS at the end of the unit.
+// work unit) and split the unit's ascending union of kept key blocks into
+// 64-key tiles: one 64-token block, or two 32-token blocks (the next two union entries, rows
+// 0-31 and 32-63 of the tile).  Group g takes tiles g, g+2, g+4, ... with its own
+// online-softmax state, and the two partial results (row maximum, row sum, O) are merged
+// through LDS at the end of the unit.
 // Each group alternates two phases separated by workgroup barriers:
 //   M_i  S_i = K_i Q^T  and  O += V_{i-1} P_{i-1}            (MFMA)
 //   X_i  loads of K_{i+2} and V_{i+1};  P_i = softmax step of S_i   (VALU)
@@ -661,9 +287,10 @@ __global__ __launch_bounds__(512, 1) void k_attn_pp(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     void *__restrict__ o, int out_f32, const int32_t *__restrict__ row_ptr, const int32_t *__restrict__ col_idx,
     const int32_t *__restrict__ worklist, int32_t *__restrict__ counter, int units, int ngroups, int nqb, int N,
-    int NKP, float sl2, uint64_t *__restrict__ trace) {
-  using C = AttnCfg<BK, D>;        // tile geometry; the 4 waves of a group load its tiles
-  static_assert(BK == 64, "64-key tiles (the merge reuses two K tiles as exchange area)");
+    float sl2, uint64_t *__restrict__ trace) {
+  using C = AttnCfg<64, D>;        // tile geometry (64 keys); the 4 waves of a group load its tiles
+  static_assert(BK == 64 || BK == 32, "64-key tiles of one or two key blocks");
+  constexpr int PB = 64 / BK;     // key blocks per tile
   constexpr int G = 128 / BQ;     // query blocks per unit
   constexpr int WPQ = BQ / 32;    // waves per query block (within a group)
   constexpr int MAXW = 40;        // kept-block bitmap words (1280 key blocks)
@@ -754,8 +381,11 @@ __global__ __launch_bounds__(512, 1) void k_attn_pp(
     // Piece i of a wave's part is 1 KB further in both the tile and LDS, so all pieces use the
     // part's LDS base with instruction offsets 1024 i.
     static_assert(C::KRPI * C::KROW == 1024 && C::KI * 1024 <= 4096, "1 KB pieces, 12-bit offsets");
+    // Wave wg loads tile rows 16 wg .. 16 wg + 15: rows 16 wg.. of the block (64-token blocks)
+    // or rows 16 (wg & 1).. of block `jb` of the tile's half wg / 2 (32-token blocks).
+    const uint32_t row_off = (uint32_t)(PB == 1 ? wg : (wg & 1)) * C::KI * C::KRPI * C::KROW;
     auto load_k = [&](int jb, uint8_t *kbuf) {
-      const uint32_t sbase = jb < 0 ? kFar : (uint32_t)jb * BK * D * 2 + (uint32_t)wg * C::KI * C::KRPI * C::KROW;
+      const uint32_t sbase = jb < 0 ? kFar : (uint32_t)jb * BK * D * 2 + row_off;
       uint8_t *dst = kbuf + wg * C::KI * 1024;
       auto piece = [&](auto ic) {
         constexpr int i = decltype(ic)::value;
@@ -774,7 +404,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_pp(
       if constexpr (C::KI > 3) piece(std::integral_constant<int, 3>{});
     };
     auto load_v = [&](int jb, uint8_t *vbuf) {
-      const uint32_t sbase = jb < 0 ? kFar : (uint32_t)jb * BK * D * 2 + (uint32_t)wg * C::KI * C::KRPI * C::KROW;
+      const uint32_t sbase = jb < 0 ? kFar : (uint32_t)jb * BK * D * 2 + row_off;
       uint8_t *dst = vbuf + wg * C::KI * 1024;
       dma16_at<0>(vrs, v_vo + sbase, dst);
       if constexpr (C::KI > 1) dma16_at<1024>(vrs, v_vo + sbase, dst);
@@ -840,21 +470,34 @@ __global__ __launch_bounds__(512, 1) void k_attn_pp(
     }
     __syncthreads();
     const int n = s_n;
-    const int S = (n + 1) >> 1;                   // steps of either group
-    auto entry = [&](int i) -> int {              // list entry of this group's step i, or -1
-      const int e = 2 * i + grp;
-      return e < n ? __builtin_amdgcn_readfirstlane(s_list[e]) : -1;
+    const int S = (n + 2 * PB - 1) / (2 * PB);   // steps (tiles) of either group
+    // List entries of a tile's key blocks (b: second block of a 32-token pair), -1 if none.
+    struct Ent {
+      int a, b;
     };
+    auto entry = [&](int i) -> Ent {              // this group's step i
+      const int e = PB * (2 * i + grp);
+      Ent r;
+      r.a = e < n ? __builtin_amdgcn_readfirstlane(s_list[e]) : -1;
+      r.b = (PB == 2 && e + 1 < n) ? __builtin_amdgcn_readfirstlane(s_list[e + 1]) : -1;
+      return r;
+    };
+    // the entry whose block this wave loads (entry -1 >> 4 = -1: an empty load)
+    auto own = [&](const Ent &e) -> int { return (PB == 2 && (wg >> 1)) ? e.b : e.a; };
+    auto keeps = [&](int e) -> bool { return e >= 0 && ((e >> wq) & 1); };
 
-    int ep = -1, ec = entry(0), e1 = entry(1);   // entries of steps i-1, i, i+1
-    // X_i needs the entry of step i+2: it is read from LDS one phase ahead, so the read's
-    // latency is spent in the M phase in between
-    auto entry_lds = [&](int i) -> int { const int e = 2 * i + grp; return e < n ? s_list[e] : -1; };
-    int enx = entry_lds(2);
+    Ent ep = {-1, -1}, ec = entry(0), e1 = entry(1);   // entries of steps i-1, i, i+1
+    // X_i needs the entries of step i+2: they are read from LDS one phase ahead, so the
+    // read's latency is spent in the M phase in between
+    auto entry_lds = [&](int i) -> Ent {
+      const int e = PB * (2 * i + grp);
+      return Ent{e < n ? s_list[e] : -1, (PB == 2 && e + 1 < n) ? s_list[e + 1] : -1};
+    };
+    Ent enx = entry_lds(2);
     // prologue in the order a previous X phase would use: K_0, then K_1 and V_0
-    load_k(ec >> 4, K0[grp]);      // (entry -1 >> 4 = -1: an empty load)
-    load_k(e1 >> 4, K1[grp]);
-    load_v(ec >> 4, V0[grp]);
+    load_k(own(ec) >> 4, K0[grp]);
+    load_k(own(e1) >> 4, K1[grp]);
+    load_v(own(ec) >> 4, V0[grp]);
 
     f16v oacc[C::NM];
 #pragma unroll
@@ -878,8 +521,8 @@ __global__ __launch_bounds__(512, 1) void k_attn_pp(
       // still be in flight
       wait_vmcnt<C::KI + C::VI>();
       lds_barrier();
-      dos = ec >= 0 && ((ec >> wq) & 1);
-      const bool dop = ep >= 0 && ((ep >> wq) & 1);
+      dos = keeps(ec.a) || keeps(ec.b);
+      const bool dop = keeps(ep.a) || keeps(ep.b);
       __builtin_amdgcn_s_setprio(2);   // MFMA issue ahead of the partner wave's VALU work
       // Consecutive MFMAs go to independent accumulators (the NKT chains of S, the NM chains
       // of O).  Operands come from a ring of RING fragments read from LDS RING MFMAs ahead;
@@ -933,20 +576,37 @@ __global__ __launch_bounds__(512, 1) void k_attn_pp(
     auto phaseX = [&](int i, uint8_t *kdst, uint8_t *vdst) {
       lds_barrier();
       // ---- X_i
-      const int e2 = __builtin_amdgcn_readfirstlane(enx);
+      const Ent e2 = {__builtin_amdgcn_readfirstlane(enx.a), __builtin_amdgcn_readfirstlane(enx.b)};
       enx = entry_lds(i + 3);
-      load_k(e2 >> 4, kdst);
-      load_v(e1 >> 4, vdst);
+      load_k(own(e2) >> 4, kdst);
+      load_v(own(e1) >> 4, vdst);
       if (dos) {
-        // online softmax (lane: query qrow; keys 32kt + 8(v/4) + 4h + v%4 of the block)
-        const int kbase = (ec >> 4) * BK;
-        if (kbase + BK > N) {
-          const int lim = N - kbase - 4 * h;
+        // online softmax (lane: query qrow; keys 32kt + 8(v/4) + 4h + v%4 of the tile)
+        if constexpr (PB == 1) {
+          const int kbase = (ec.a >> 4) * BK;
+          if (kbase + BK > N) {
+            const int lim = N - kbase - 4 * h;
 #pragma unroll
-          for (int kt = 0; kt < C::NKT; ++kt)
+            for (int kt = 0; kt < C::NKT; ++kt)
 #pragma unroll
-            for (int v = 0; v < 16; ++v)
-              if (32 * kt + 8 * (v >> 2) + (v & 3) >= lim) sacc[kt][v] = -INFINITY;
+              for (int v = 0; v < 16; ++v)
+                if (32 * kt + 8 * (v >> 2) + (v & 3) >= lim) sacc[kt][v] = -INFINITY;
+          }
+        } else {
+          // 32-key half kt holds block (kt ? b : a): masked whole when this wave's query block
+          // did not keep it (or it is absent), and past N when it is the ragged last block
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt) {
+            const int e = kt ? ec.b : ec.a;
+            const bool kp = keeps(e);
+            const int kbase = kp ? (e >> 4) * BK : 0;
+            if (!kp || kbase + BK > N) {
+              const int lim = kp ? N - kbase - 4 * h : -64;
+#pragma unroll
+              for (int v = 0; v < 16; ++v)
+                if (8 * (v >> 2) + (v & 3) >= lim) sacc[kt][v] = -INFINITY;
+            }
+          }
         }
         float mloc = sacc[0][0];
 #pragma unroll
@@ -1158,13 +818,6 @@ __global__ __launch_bounds__(BQ) void k_attn_f32(const float *__restrict__ q, co
 // ---------------------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------------------
-int launch_vt(const void *v, void *vt, int BH, int N, int D, int NKP, hipStream_t st) {
-  hipLaunchKernelGGL(k_vt, dim3(NKP / 64, D / 64, BH), dim3(256), 0, st, (const uint16_t *)v, (uint16_t *)vt, N,
-                     D, NKP);
-  FV_CHECK_LAUNCH();
-  return FVATTN_OK;
-}
-
 int launch_worklist(const int32_t *row_ptr, int rows, int nqb, int nkb, int G, int sched, int32_t *wl,
                     int32_t *counter, hipStream_t st) {
   hipLaunchKernelGGL(k_worklist, dim3(1), dim3(1024), 0, st, row_ptr, rows, nqb, nkb, G, sched, wl, counter);
@@ -1173,13 +826,12 @@ int launch_worklist(const int32_t *row_ptr, int rows, int nqb, int nkb, int G, i
 }
 
 template <int BQ, int BK, int D>
-static int launch_attn_bf16_t(const void *q, const void *k, const void *v, const void *vt, void *o, int out_f32,
+static int launch_attn_bf16_t(const void *q, const void *k, const void *v, void *o, int out_f32,
                               const int32_t *row_ptr, const int32_t *col_idx, const int32_t *wl, int32_t *counter,
-                              int rows, int nqb, int N, int NKP, int grid, uint64_t *trace, hipStream_t st) {
-  // 64-key blocks: two wave groups per unit (k_attn_pp), V as given; 32-key blocks: k_attn_bf16
-  // over the transposed copy of V
-  auto kern = BK == 64 ? k_attn_pp<BQ, 64, D> : k_attn_bf16<BQ, BK, D>;
-  const int nthreads = BK == 64 ? 512 : 256;
+                              int rows, int nqb, int N, int grid, uint64_t *trace, hipStream_t st) {
+  // two wave groups per unit (k_attn_pp), V as given
+  auto kern = k_attn_pp<BQ, BK, D>;
+  const int nthreads = 512;
   constexpr int G = 128 / BQ;
   const int ngroups = (nqb + G - 1) / G;
   const int units = (rows / nqb) * ngroups;
@@ -1192,21 +844,20 @@ static int launch_attn_bf16_t(const void *q, const void *k, const void *v, const
   if (grid > units) grid = units;
   const float sl2 = (float)(1.4426950408889634 / sqrt((double)D));
   hipLaunchKernelGGL(kern, dim3(grid), dim3(nthreads), 0, st, (const uint16_t *)q, (const uint16_t *)k,
-                     (const uint16_t *)(BK == 64 ? v : vt), o, out_f32, row_ptr, col_idx, wl, counter, units, ngroups,
-                     nqb, N, NKP,
-                     sl2, trace);
+                     (const uint16_t *)v, o, out_f32, row_ptr, col_idx, wl, counter, units, ngroups,
+                     nqb, N, sl2, trace);
   FV_CHECK_LAUNCH();
   return FVATTN_OK;
 }
 
-int launch_attn_bf16(const void *q, const void *k, const void *v, const void *vt, void *o, int out_f32,
+int launch_attn_bf16(const void *q, const void *k, const void *v, void *o, int out_f32,
                      const int32_t *row_ptr,
-                     const int32_t *col_idx, const int32_t *wl, int32_t *counter, int rows, int nqb, int N, int NKP,
+                     const int32_t *col_idx, const int32_t *wl, int32_t *counter, int rows, int nqb, int N,
                      int D, int BQ, int BK, int grid, uint64_t *trace, hipStream_t st) {
 #define FV_A(bq, bk, dd)                                                                                 \
   if (BQ == bq && BK == bk && D == dd)                                                                   \
-    return launch_attn_bf16_t<bq, bk, dd>(q, k, v, vt, o, out_f32, row_ptr, col_idx, wl, counter, rows, nqb, N, \
-                                          NKP, grid, trace, st);
+    return launch_attn_bf16_t<bq, bk, dd>(q, k, v, o, out_f32, row_ptr, col_idx, wl, counter, rows, nqb, N, \
+                                          grid, trace, st);
   FV_A(64, 64, 128) FV_A(128, 64, 128) FV_A(32, 64, 128) FV_A(64, 32, 128) FV_A(128, 32, 128) FV_A(32, 32, 128)
   FV_A(64, 64, 64) FV_A(128, 64, 64) FV_A(32, 64, 64) FV_A(64, 32, 64) FV_A(128, 32, 64) FV_A(32, 32, 64)
 #undef FV_A

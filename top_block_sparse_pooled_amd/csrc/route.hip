@@ -681,7 +681,7 @@ static int launch_select_mt(const void *q, const double *ksw, int BH, int nqb, i
 }
 
 // Key tiles (of 16 blocks) per wave: up to 512 key blocks run on 4 waves with at most 8 tiles
-// each; more (up to 1280) on 8 waves with at most 10 tiles each.
+// each; more on 8 waves with 8 tiles each (up to 1024) or 10 (up to 1280).
 template <typename T, int D>
 static int launch_select_d(const void *q, const double *ksw, int BH, int nqb, int nkb, double p, int32_t *counts,
                            uint32_t *bitmask, int nkw, int32_t *head_load, int32_t *bsum, const SelOpts &sel,
@@ -693,6 +693,7 @@ static int launch_select_d(const void *q, const double *ksw, int BH, int nqb, in
   if (nkt <= 8) FV_SEL(2, 4);
   if (nkt <= 16) FV_SEL(4, 4);
   if (nkt <= 32) FV_SEL(8, 4);
+  if (nkt <= 64) FV_SEL(8, 8);
   FV_SEL(10, 8);
 #undef FV_SEL
 }

@@ -92,6 +92,10 @@ WORKLOADS = {
         # 720p-shaped layer (40 heads, 21 x 45 x 80 latent tokens)
         Workload("wan14b_n75600", H=40, T=21, Y=45, X=80, d=128, block_q=64, block_k=64,
                  ps=(0.9,), dtype="bf16", alpha=("uniform", 0.0, 3.0), seed=1004),
+        # the benchmark layer routed and attended with 32-token key blocks (the pages allow
+        # blocks of 32 or 64 tokens)
+        Workload("wan14b_n32760_bk32", H=40, T=21, Y=30, X=52, d=128, block_q=64, block_k=32,
+                 ps=(0.9,), dtype="bf16", alpha=("uniform", 0.0, 4.0), seed=1003),
         # load-skew stress: q-block 128, k-block 64, per-head alpha log-uniform
         Workload("skew_n75600_bq128", H=40, T=21, Y=45, X=80, d=128, block_q=128, block_k=64,
                  ps=(0.95,), dtype="bf16", alpha=("loguniform", 0.1, 6.0), seed=1005),
