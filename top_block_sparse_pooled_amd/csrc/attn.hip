@@ -302,7 +302,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_pp(
   __shared__ __attribute__((aligned(1024))) uint8_t V1[2][C::VBYTES];
   __shared__ uint32_t s_bm[G + 1][MAXW];   // kept key blocks of each query block; row G: union
   __shared__ int s_list[MAXW * 32];        // union, ascending: (key block << 4) | keeping query blocks
-  __shared__ int s_wpre[MAXW];             // union blocks before each bitmap word
+  __shared__ int s_cpre[PB == 2 ? (1 << G) - 1 : 1][MAXW];   // list position of each class's word
   __shared__ float s_xm[2][4][64], s_xl[2][4][64];
   __shared__ int s_n, s_tile;
   static_assert(2 * C::KBYTES >= 4 * NH * 16 * 64 * 4, "exchange area");
@@ -444,19 +444,34 @@ __global__ __launch_bounds__(512, 1) void k_attn_pp(
       atomicOr(&s_bm[G][j >> 5], 1u << (j & 31));
     }
     __syncthreads();
-    // union list, ascending: word prefix counts by one wave, then every thread places the
-    // blocks of its own key positions
-    if (w == 0) {
-      const uint32_t word = lane < nkw ? s_bm[G][lane] : 0u;
-      const int pc = __popc(word);
-      int incl = pc;
+    // union list: word prefix counts by one wave, then every thread places the blocks of its
+    // own key positions.  64-token blocks: ascending.  32-token blocks: grouped by the set of
+    // query blocks that kept them (ascending within a set, sets in increasing mask order), so
+    // the two blocks of a tile are kept by the same waves, which compute it whole or skip it.
+    constexpr int NCLS = PB == 2 ? (1 << G) - 1 : 1;
+    auto class_word = [&](int c, int x) -> uint32_t {   // blocks of word x in class c
+      uint32_t cw = s_bm[G][x];
+      if constexpr (PB == 2) {
 #pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int ov = __shfl_up(incl, off);
-        if (lane >= off) incl += ov;
+        for (int gi = 0; gi < G; ++gi) cw &= (((c + 1) >> gi) & 1) ? s_bm[gi][x] : ~s_bm[gi][x];
       }
-      if (lane < MAXW) s_wpre[lane] = incl - pc;
-      if (lane == 63) s_n = incl;
+      return cw;
+    };
+    if (w == 0) {
+      int base = 0;
+      for (int c = 0; c < NCLS; ++c) {
+        const uint32_t word = lane < nkw ? class_word(c, lane) : 0u;
+        const int pc = __popc(word);
+        int incl = pc;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const int ov = __shfl_up(incl, off);
+          if (lane >= off) incl += ov;
+        }
+        if (lane < MAXW) s_cpre[c][lane] = base + incl - pc;
+        base += __shfl(incl, 63);
+      }
+      if (lane == 0) s_n = base;
     }
     __syncthreads();
     for (int j = tid; j < nkw * 32; j += NTH) {
@@ -465,7 +480,8 @@ __global__ __launch_bounds__(512, 1) void k_attn_pp(
         int msk = 0;
 #pragma unroll
         for (int gi = 0; gi < G; ++gi) msk |= (int)((s_bm[gi][j >> 5] >> (j & 31)) & 1u) << gi;
-        s_list[s_wpre[j >> 5] + __popc(word & ((1u << (j & 31)) - 1u))] = (j << 4) | msk;
+        const int c = PB == 2 ? msk - 1 : 0;
+        s_list[s_cpre[c][j >> 5] + __popc(class_word(c, j >> 5) & ((1u << (j & 31)) - 1u))] = (j << 4) | msk;
       }
     }
     __syncthreads();
