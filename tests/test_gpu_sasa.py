@@ -116,6 +116,8 @@ CASES = [
                                                          "bf16", (5, 20, 20)), 0.9),
     ("f32_h4_n1000_d64", lambda: workloads.small_case(4, 1000, 64, 32, 32, 53, ("uniform", 0.0, 3.0), "f32",
                                                       (4, 10, 25)), 0.8),
+    ("bf16_h2_n22050_bk32_nkb690", lambda: workloads.small_case(2, 22050, 128, 64, 32, 54, ("uniform", 0.0, 3.5),
+                                                                "bf16", (21, 30, 35)), 0.85),
 ]
 SETTINGS = [
     ("g2_a0.5", dict(groups=2, alpha=0.5, tau=0.0), {}),

@@ -51,6 +51,8 @@ CASES = [
                                                              "bf16", (3, 10, 50))),
     ("f32_h2_n1000_d64", lambda: workloads.small_case(2, 1000, 64, 64, 64, 44, ("uniform", 0.0, 3.0),
                                                       "f32", (4, 10, 25))),
+    ("bf16_h1_n22050_bk32_nkb690", lambda: workloads.small_case(1, 22050, 128, 64, 32, 46, ("uniform", 0.0, 3.0),
+                                                                "bf16", (21, 30, 35))),
     ("bf16_h1_n75600_nkb1182", lambda: workloads.small_case(1, 75600, 128, 64, 64, 45, ("uniform", 0.0, 3.0),
                                                             "bf16", (21, 45, 80))),
 ]
