@@ -9,9 +9,9 @@
 //  * a work unit is 128 query rows = 128/BQ adjacent query blocks of one head; a persistent
 //    grid of workgroups pops units from a device work list through an atomic ticket, so the
 //    order (identity, heaviest first, ...) is the plan's choice;
-//  * the unit walks the ascending union of its query blocks' kept key blocks; each block's K
-//    and V tiles go into LDS once, straight from global memory (buffer_load ... lds), and every
-//    wave whose query block kept the block uses them;
+//  * the unit walks the union of its query blocks' kept key blocks; each block's K and V
+//    tiles go into LDS once, straight from global memory (buffer_load ... lds), and every wave
+//    whose query block kept the block uses them;
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (K from LDS as operand A, Q in registers as
 //    operand B), so each lane owns one query column and the softmax row statistics need one
 //    cross-half exchange (v_permlane32_swap) per block;
@@ -257,9 +257,10 @@ __device__ __forceinline__ uint64_t hw_id_word() {
 // bf16 MFMA attention, two wave groups per unit (k_attn_pp).
 //
 // A workgroup is 8 waves in two groups of 4.  Both groups cover the same 128 query rows (one
-// work unit) and split the unit's ascending union of kept key blocks into
-// 64-key tiles: one 64-token block, or two 32-token blocks (the next two union entries, rows
-// 0-31 and 32-63 of the tile).  Group g takes tiles g, g+2, g+4, ... with its own
+// work unit) and split the unit's union of kept key blocks into 64-key tiles: one 64-token
+// block, or two 32-token blocks (the next two union entries, rows 0-31 and 32-63 of the
+// tile; the union is then ordered by the query blocks that kept each block, so both blocks of
+// a tile serve the same waves).  Group g takes tiles g, g+2, g+4, ... with its own
 // online-softmax state, and the two partial results (row maximum, row sum, O) are merged
 // through LDS at the end of the unit.
 // Each group alternates two phases separated by workgroup barriers:
