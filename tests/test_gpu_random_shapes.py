@@ -35,7 +35,7 @@ def to_dev(x, dtype):
     return t.to(DEV).contiguous()
 
 
-def _draw_cases(n=10, seed=20261203):
+def _draw_cases(n=16, seed=20261203):
     rng = np.random.default_rng(seed)
     cases = []
     for i in range(n):
@@ -45,6 +45,8 @@ def _draw_cases(n=10, seed=20261203):
         T, Y, X = int(rng.integers(1, 6)), int(rng.integers(1, 18)), int(rng.integers(1, 26))
         if i == 0:
             T, Y, X = 1, 1, 23          # shorter than any block
+        if i >= 10:
+            T, Y, X = T + 2, Y + 15, X + 20   # larger grids: many tiles per unit, ragged tails
         N = T * Y * X
         H = int(rng.integers(1, 4))
         p = 1.0 if i == 1 else round(float(rng.uniform(0.5, 0.99)), 3)
