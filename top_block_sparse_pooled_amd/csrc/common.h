@@ -1,6 +1,8 @@
 // Shared definitions of the gfx950 kernels: vector types, bf16 conversions, launch checks.
 #pragma once
 #include <hip/hip_runtime.h>
+
+#include <atomic>
 #include <stdint.h>
 
 #include "fvattn.h"
@@ -57,16 +59,20 @@ __device__ __forceinline__ int digit_shift(unsigned long long width) {
 
 // Compute units of the current device (cached per device); 0 on success.
 inline int device_cus(int *cus) {
-  static int cache[64] = {0};
+  // per-device cache; concurrent callers may both query and store the same value
+  static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return -1;
-  if (dev >= 0 && dev < 64 && cache[dev] > 0) {
-    *cus = cache[dev];
-    return 0;
+  if (dev >= 0 && dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) {
+      *cus = c;
+      return 0;
+    }
   }
   int n = 0;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return -1;
-  if (dev >= 0 && dev < 64) cache[dev] = n;
+  if (dev >= 0 && dev < 64) cache[dev].store(n, std::memory_order_relaxed);
   *cus = n;
   return 0;
 }
