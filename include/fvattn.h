@@ -85,8 +85,10 @@ typedef struct fvattn_csr {
 } fvattn_csr;
 
 /*
- * Options of fvattn_sparse_attn; pass NULL for the defaults (LPT order, library grid,
- * no trace).
+ * Options of fvattn_sparse_attn; pass NULL for the defaults (identity order, library grid,
+ * no trace).  The identity order is the fastest measured on MI355X: with one workgroup per
+ * CU, the units in flight are those of one head, whose K/V tiles then share the caches.
+ * LPT balances the per-CU load best but mixes heads.
  *   schedule  one of FVATTN_SCHED_*.
  *   grid      number of persistent workgroups; 0 = as many as stay resident.
  *   trace     optional device array [rows * 4] of uint64.  Record t (t < units) describes the

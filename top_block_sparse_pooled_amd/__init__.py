@@ -295,7 +295,7 @@ def worklist(csr: Csr, schedule: str = "lpt", with_counter: bool = False):
     return (wl, ctr) if with_counter else wl
 
 
-def sparse_attn(q, k, v, csr: Csr, schedule: str = "lpt", grid: int = 0, trace=None, out=None, ws=None,
+def sparse_attn(q, k, v, csr: Csr, schedule: str = "identity", grid: int = 0, trace=None, out=None, ws=None,
                 out_dtype=None):
     """Block-sparse attention over the CSR's kept blocks -> o [B, H, N, d].
     out_dtype: None (dtype of q) or torch.float32 (accumulator precision, for bf16 inputs)."""
@@ -336,7 +336,7 @@ def attn_ws(q, csr: Csr):
     return torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
 
 
-def attn_plan(v, csr: Csr, ws, schedule: str = "lpt"):
+def attn_plan(v, csr: Csr, ws, schedule: str = "identity"):
     """Work list of the CSR rows into ws (v supplies the shape only); see fvattn_attn_plan."""
     _check_qkv(v)
     B, H, N, d = v.shape

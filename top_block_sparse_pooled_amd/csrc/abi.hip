@@ -374,7 +374,7 @@ int fvattn_sparse_attn(const void *q, const void *k, const void *v, void *o, int
   AttnWs w;
   int rc = attn_checks(v, B, H, N, d, dtype, csr, &s, ws, ws_bytes, &w);
   if (rc != FVATTN_OK) return rc;
-  const int sched = opts ? opts->schedule : FVATTN_SCHED_LPT;
+  const int sched = opts ? opts->schedule : FVATTN_SCHED_IDENTITY;
   if ((rc = sched_ok(sched, s)) != FVATTN_OK) return rc;
   int grid, out_dt;
   uint64_t *trace;
