@@ -80,6 +80,10 @@ SMALL = [
                                                        "bf16", (5, 20, 21)), 0.9),
     ("bf16_h2_n1800_bq32", lambda: workloads.small_case(2, 1800, 128, 32, 64, 29, ("uniform", 0.5, 3.0),
                                                         "bf16", (3, 20, 30)), 0.85),
+    ("bf16_h2_n3000_p1e-6", lambda: workloads.small_case(2, 3000, 128, 64, 64, 32, ("uniform", 0.0, 3.0),
+                                                         "bf16", (3, 20, 50)), 1e-6),
+    ("bf16_h2_n3000_p0.999999", lambda: workloads.small_case(2, 3000, 128, 64, 64, 33, ("uniform", 0.0, 3.0),
+                                                             "bf16", (3, 20, 50)), 0.999999),
     ("bf16_h1_n32760_bk32_nkb1024", lambda: workloads.small_case(1, 32760, 128, 64, 32, 30, ("uniform", 0.0, 4.0),
                                                                  "bf16", (21, 30, 52)), 0.9),
     ("bf16_h2_n22050_bk32_nkb690", lambda: workloads.small_case(2, 22050, 128, 64, 32, 31, ("uniform", 0.0, 3.0),
