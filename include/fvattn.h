@@ -263,7 +263,8 @@ int fvattn_sparse_attn(const void *q, const void *k, const void *v, void *o, int
  * First half of fvattn_sparse_attn: builds the work list of the CSR rows in `schedule`
  * order in `ws`.  The attention kernel reads q, k and v as given, so the plan depends on the
  * CSR only: it stays valid while the CSR and ws are unchanged, whatever q, k, v it later
- * meets.  v is not read (the argument keeps the signature of fvattn_sparse_attn's inputs).
+ * meets.  v is not read; it must be non-NULL (the argument keeps the signature of
+ * fvattn_sparse_attn's inputs).
  */
 int fvattn_attn_plan(const void *v, int B, int H, int N, int d, int dtype, const fvattn_csr *csr,
                      int schedule, void *ws, size_t ws_bytes, void *stream);
