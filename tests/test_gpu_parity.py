@@ -262,8 +262,8 @@ def test_determinism_schedule_independence_and_trace():
 
 
 # ------------------------------------------------------------------ full-size workloads
-FULL = [("wan1p3b_n32760", 0.9), ("wan14b_n32760", 0.90), ("wan14b_n32760", 0.95), ("wan14b_n75600", 0.9),
-        ("skew_n75600_bq128", 0.95)]
+FULL = [("wan1p3b_n32760", 0.9), ("wan14b_n32760", 0.90), ("wan14b_n32760", 0.95), ("wan14b_n32760", 1.0),
+        ("wan14b_n32760_bk32", 0.9), ("wan14b_n75600", 0.9), ("skew_n75600_bq128", 0.95)]
 
 
 def _sample_heads(w):
