@@ -544,7 +544,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_pp(
       // Consecutive MFMAs go to independent accumulators (the NKT chains of S, the NM chains
       // of O).  Operands come from a ring of RING fragments read from LDS RING MFMAs ahead;
       // sched_barrier keeps the compiler from sinking the reads back to their uses.
-      constexpr int RING = 4;
+      constexpr int RING = 3;
       if (dos) {
         constexpr int NT_S = C::NS * C::NKT;   // MFMA t: k-step t / NKT, key tile t % NKT
         auto kaddr = [&](int t) {
