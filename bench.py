@@ -22,6 +22,7 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
+SCHEDULES = ("lpt", "identity", "head_lpt", "xcd", "rlb", "head_desc")
 METRIC = "sparse-attn effective TFLOP/s (executed blocks) + ms/layer at N=32760 H=40 d=128"
 
 
@@ -112,7 +113,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="wan14b_n32760")
     ap.add_argument("--p", type=float, default=None)
-    ap.add_argument("--schedule", default="identity", choices=["lpt", "identity", "head_lpt", "xcd"])
+    ap.add_argument("--schedule", default="identity", choices=sorted(SCHEDULES))
+    ap.add_argument("--alt-p", type=float, default=0.95,
+                    help="also time the layer at this p (the workload's second threshold); 0: off")
     ap.add_argument("--out", default="bf16", choices=["f32", "bf16"],
                     help="output dtype of the attention: bf16 (the layer's output, rounded to nearest even) or "
                          "f32 (accumulator precision)")
@@ -220,6 +223,38 @@ def main():
     log(f"[bench] ms/step {ms_step:.3f} (route {route_ms:.3f}, plan {plan_ms:.3f}, attn {attn_ms:.3f}); "
         f"attn {attn_tflops:.1f} TFLOP/s; route {route_gbps:.0f} GB/s; kept {nnz / (w.rows * w.nkb):.4f}")
 
+    alt = None
+    if args.alt_p and args.alt_p != p and args.mode == "topp" and args.sasa_groups == 0 and args.route_every == 1:
+        # the same layer at the workload's other threshold (a few timed steps, after the main timing)
+        ev2 = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(5)]
+        csr2 = fv.Csr.empty(1, w.H, w.N, w.block_q, w.block_k, dev)
+
+        def step2(ev):
+            ev[0].record()
+            fv.route(qd, kd, w.block_q, w.block_k, args.alt_p, csr=csr2, ws=rws, **variant)
+            ev[1].record()
+            fv.attn_plan(vd, csr2, aws, args.schedule)
+            ev[2].record()
+            fv.attn_run(qd, kd, vd, csr2, aws, out=o, out_dtype=out_dtype)
+            ev[3].record()
+
+        step2(ev2[0])
+        torch.cuda.synchronize()
+        for e in ev2:
+            step2(e)
+        torch.cuda.synchronize()
+        rp2 = csr2.row_ptr.cpu().numpy().astype(np.int64)
+        ci2 = csr2.col_idx[: int(rp2[-1])].cpu().numpy().astype(np.int64)
+        fl2, _ = executed_flops(rp2, ci2, w.N, w.nqb, w.block_q, w.block_k, w.d)
+        ms = [e[0].elapsed_time(e[3]) for e in ev2]
+        a_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev2]))
+        alt = dict(p=args.alt_p, ms_per_layer=float(np.mean(ms)), route_ms=float(np.mean([e[0].elapsed_time(e[1])
+                                                                                          for e in ev2])),
+                   attn_ms=a_ms, attn_tflops=fl2 / (a_ms * 1e-3) / 1e12, executed_tflop=fl2 / 1e12,
+                   kept_frac=float(rp2[-1]) / (w.rows * w.nkb), steps=len(ev2))
+        log(f"[bench] p={args.alt_p}: {json.dumps(alt)}")
+        del csr2
+
     sasa_info = None
     if args.sasa_groups > 0:
         R = args.sasa_groups
@@ -251,7 +286,7 @@ def main():
     extras = {}
     if not args.no_extras:
         bal = {}
-        for sched in ("lpt", "identity", "head_lpt", "xcd"):
+        for sched in SCHEDULES:
             tr = torch.zeros(w.rows * 4, dtype=torch.int64, device=dev)
             fv.attn_plan(vd, csr, aws, sched)
             fv.attn_run(qd, kd, vd, csr, aws, out=o, out_dtype=out_dtype, trace=tr)
@@ -306,6 +341,7 @@ def main():
         routing=dict(bound="hbm", achieved=route_gbps, peak=PEAK_HBM_GBPS, unit="GB/s",
                      frac=route_gbps / PEAK_HBM_GBPS, algorithmic_bytes=route_bytes, us=1e3 * route_ms),
         cpu_baseline=cpu,
+        layer_alt_p=alt,
         **extras,
     )
     print(json.dumps(rec), flush=True)

@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define FVATTN_VERSION 10000 /* 1.0.0 */
+#define FVATTN_VERSION 10100 /* 1.1.0 */
 
 typedef enum fvattn_dtype { FVATTN_BF16 = 0, FVATTN_F32 = 1 } fvattn_dtype;
 
@@ -51,14 +51,35 @@ enum {
   FVATTN_ERR_MISMATCH = -7     /* CSR shape fields do not match the attention arguments       */
 };
 
-/* Work-list orders for fvattn_worklist / fvattn_sparse_attn. */
+/*
+ * Work-list orders for fvattn_worklist / fvattn_attn_plan / fvattn_sparse_attn.  A work unit is
+ * G adjacent query blocks of one head; its work is the number of (query block, key block) pairs
+ * its rows keep.  Head loads are the per-head loads of the FVAttn summary's RLB section.
+ */
 enum {
-  FVATTN_SCHED_LPT = 0,      /* rows by kept-block count, longest first, ties by row id    */
-  FVATTN_SCHED_IDENTITY = 1, /* rows in ascending id (head-major) order                     */
-  FVATTN_SCHED_HEAD_LPT = 2, /* heads by load (heaviest first), rows of a head longest first */
-  FVATTN_SCHED_XCD = 3       /* rows in id order cut into 8 contiguous ranges of equal kept-block
-                                work, one per XCD (shared L2); an XCD that runs out takes rows
-                                from the others                                              */
+  FVATTN_SCHED_LPT = 0,      /* units by work, longest first, ties by unit id                 */
+  FVATTN_SCHED_IDENTITY = 1, /* units in ascending id (head-major) order                      */
+  FVATTN_SCHED_HEAD_LPT = 2, /* heads by load (heaviest first, ties by id), a head's units
+                                longest first                                                 */
+  FVATTN_SCHED_XCD = 3,      /* units in id order cut into 8 contiguous ranges of equal work, one
+                                per XCD (shared L2); an XCD that runs out takes units from the
+                                others                                                        */
+  FVATTN_SCHED_RLB = 4,      /* heads by load (heaviest first) each assigned to the XCD queue with
+                                the least load so far (ties: lower XCD); a queue holds its heads in
+                                assignment order, a head's units in id order; stealing as XCD.
+                                The summary's RLB moves the heaviest heads first between ranks;
+                                here the ranks are the 8 XCDs                                  */
+  FVATTN_SCHED_HEAD_DESC = 5 /* heads by load (heaviest first, ties by id), a head's units in id
+                                order, one queue                                               */
+};
+
+/* Bits of the device status words read by fvattn_ws_status (0 = no internal error). */
+enum {
+  FVATTN_STATUS_SELECT_NOCROSS = 1, /* routing: a row's radix search found no bin where the
+                                       cumulative mass crosses its target; that row was kept
+                                       whole.  Not expected to occur: an internal error.    */
+  FVATTN_STATUS_PLAN_MISMATCH = 2   /* attention: the plan in the workspace was built for another
+                                       dtype, CSR shape or unit size; nothing was computed    */
 };
 
 /*
@@ -91,12 +112,14 @@ typedef struct fvattn_csr {
  * LPT balances the per-CU load best but mixes heads.
  *   schedule  one of FVATTN_SCHED_*.
  *   grid      number of persistent workgroups; 0 = as many as stay resident.
- *   trace     optional device array [rows * 4] of uint64.  Record t (t < units) describes the
- *             t-th work unit taken: {hardware id (XCC_ID << 32 | HW_ID), start clock, end clock,
- *             unit id}, clocks from the 100 MHz constant-rate counter.  A unit is 128/block_q
- *             adjacent query blocks of one head for bf16 (128 query rows) and one query block for
- *             float32; units = B*H*ceil(nqb/(128/block_q)) resp. B*H*nqb.  Records past `units`
- *             are not written.  Used to measure per-CU busy time; costs a few stores per unit.
+ *   trace     optional device array of uint64.  Record t (t < units) describes the t-th work
+ *             unit taken: {hardware id (XCC_ID << 32 | HW_ID), start clock, end clock, unit id},
+ *             clocks from the 100 MHz constant-rate counter.  A unit is 128/block_q adjacent
+ *             query blocks of one head for bf16 (128 query rows) and one query block for float32;
+ *             units = B*H*ceil(nqb/(128/block_q)) resp. B*H*nqb.  Used to measure per-CU busy
+ *             time; costs a few stores per unit.
+ *   trace_cap uint64 elements available at trace; must be >= 4 * units when trace is not NULL
+ *             (else FVATTN_ERR_INVALID).
  *   out_dtype element type of o: -1 = the input dtype; FVATTN_F32 = float32 output (the
  *             accumulator precision) for bf16 inputs.  With a bf16 output each value is the
  *             round-to-nearest-even of the float32 result.
@@ -105,6 +128,7 @@ typedef struct fvattn_attn_opts {
   int32_t schedule;
   int32_t grid;
   uint64_t *trace;
+  int64_t trace_cap;
   int32_t out_dtype;
   int32_t reserved;
 } fvattn_attn_opts;
@@ -230,15 +254,29 @@ int fvattn_route_sasa(const void *q, const void *k, int B, int H, int N, int d, 
                       int block_k, const fvattn_route_opts *ropts, const fvattn_sasa_opts *sopts,
                       fvattn_csr *csr, void *ws, size_t ws_bytes, void *stream);
 
+/* Bytes of workspace fvattn_worklist needs for `rows` CSR rows (0 if rows <= 0). */
+size_t fvattn_worklist_ws_bytes(int rows);
+
 /*
  * Device-built work list (one-GPU analogue of the FVAttn summary's runtime load balancing:
- * the heaviest work is placed first).  worklist: device int32 [rows] receives a permutation
- * of the rows in the requested FVATTN_SCHED_* order.  counter (optional, may be NULL):
- * device int32[64] control block of a persistent consumer (tickets, exit count and, for
- * FVATTN_SCHED_XCD, the per-XCD row ranges), initialised by this call.
+ * the heaviest work is placed first).  Units of G adjacent query blocks of one head (G = 1: CSR
+ * rows; the bf16 attention kernel uses G = 128 / block_q).  worklist: device int32
+ * [B*H*ceil(nqb/G)] receives a permutation of the units in the requested FVATTN_SCHED_* order.
+ * ws: device workspace of fvattn_worklist_ws_bytes(rows) bytes; its first 64 int32 are the
+ * control block of a persistent consumer (tickets; for FVATTN_SCHED_XCD and FVATTN_SCHED_RLB
+ * the per-XCD queue starts at int32 16 + x, x = 0..8).  G in {1, 2, 4}; the head-ordered
+ * schedules (HEAD_LPT, RLB, HEAD_DESC) support up to 4096 heads.
  */
-int fvattn_worklist(const fvattn_csr *csr, int schedule, int32_t *worklist, int32_t *counter,
+int fvattn_worklist(const fvattn_csr *csr, int schedule, int G, int32_t *worklist, void *ws, size_t ws_bytes,
                     void *stream);
+
+/*
+ * Status word left in a workspace by the last call that used it (FVATTN_STATUS_* bits; 0 = no
+ * internal error).  which = 0: a routing workspace (fvattn_route, _ex, _sasa); which = 1: an
+ * attention workspace (fvattn_attn_plan / _run / fvattn_sparse_attn).  Copies 4 bytes to the host
+ * and synchronises `stream`.
+ */
+int fvattn_ws_status(const void *ws, int which, uint32_t *status, void *stream);
 
 /*
  * Block-sparse attention (FVAttn summary: attention runs only over the kept blocks; the

@@ -8,5 +8,6 @@ from .topp_oracle import (  # noqa: F401
     block_bounds, pool_blocks, block_scores, block_importance, routing_order,
     topp_count, route_head, route, sparse_attention_rows, sparse_attention,
     dense_attention, lpt_worklist, csr_rows, selection_count, window_blocks, sasa_augment,
-    route_sasa, sasa_budget,
+    route_sasa, sasa_budget, unit_work, head_loads, lpt_units, heads_by_load, head_lpt_units,
+    head_desc_units, rlb_assign, rlb_units,
 )

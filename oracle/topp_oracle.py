@@ -266,6 +266,89 @@ def lpt_worklist(row_ptr: np.ndarray) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
+# Work units of the attention and their orders ([FVAttn] RLB section: a
+# head's load is the number of blocks it must compute; the balancer moves the
+# heaviest heads first, each to the least loaded rank).  A unit is G adjacent
+# query blocks of one head (G = 1: one CSR row); unit u = head * ngroups + g
+# holds query blocks g*G .. min(g*G + G, nqb) - 1 of its head, and its work is
+# the number of kept (query block, key block) pairs of those rows.
+# --------------------------------------------------------------------------
+def unit_work(row_ptr: np.ndarray, nqb: int, G: int) -> np.ndarray:
+    counts = np.diff(np.asarray(row_ptr, dtype=np.int64))
+    nh = counts.size // nqb
+    ngroups = -(-nqb // G)
+    work = np.zeros(nh * ngroups, dtype=np.int64)
+    for h in range(nh):
+        for g in range(ngroups):
+            work[h * ngroups + g] = counts[h * nqb + g * G: h * nqb + min(g * G + G, nqb)].sum()
+    return work
+
+
+def head_loads(row_ptr: np.ndarray, nqb: int) -> np.ndarray:
+    counts = np.diff(np.asarray(row_ptr, dtype=np.int64))
+    return counts.reshape(-1, nqb).sum(axis=1)
+
+
+def lpt_units(row_ptr: np.ndarray, nqb: int, G: int) -> np.ndarray:
+    """Units by work, heaviest first; equal work keeps ascending unit id."""
+    return np.argsort(-unit_work(row_ptr, nqb, G), kind="stable").astype(np.int64)
+
+
+def heads_by_load(row_ptr: np.ndarray, nqb: int) -> np.ndarray:
+    """Heads by load, heaviest first; equal loads keep ascending head id."""
+    return np.argsort(-head_loads(row_ptr, nqb), kind="stable").astype(np.int64)
+
+
+def head_lpt_units(row_ptr: np.ndarray, nqb: int, G: int) -> np.ndarray:
+    """Heads heaviest first; within a head its units heaviest first (ties by id)."""
+    work = unit_work(row_ptr, nqb, G)
+    ngroups = -(-nqb // G)
+    out = []
+    for h in heads_by_load(row_ptr, nqb):
+        us = np.arange(h * ngroups, (h + 1) * ngroups)
+        out.extend(us[np.argsort(-work[us], kind="stable")].tolist())
+    return np.array(out, dtype=np.int64)
+
+
+def head_desc_units(row_ptr: np.ndarray, nqb: int, G: int) -> np.ndarray:
+    """Heads heaviest first; a head's units in id order."""
+    ngroups = -(-nqb // G)
+    return np.array([h * ngroups + g for h in heads_by_load(row_ptr, nqb) for g in range(ngroups)],
+                    dtype=np.int64)
+
+
+def rlb_assign(loads: np.ndarray, n_bins: int):
+    """Greedy of the RLB section on one machine: heads taken heaviest first (ties:
+    lower id), each given to the bin (rank) with the least load so far (ties: lower
+    bin).  Returns (bin of each head, list per bin of its heads in assignment order)."""
+    loads = np.asarray(loads, dtype=np.int64)
+    bin_load = [0] * n_bins
+    bins = [[] for _ in range(n_bins)]
+    where = np.zeros(loads.size, dtype=np.int64)
+    for h in np.argsort(-loads, kind="stable"):
+        b = min(range(n_bins), key=lambda x: (bin_load[x], x))
+        bins[b].append(int(h))
+        bin_load[b] += int(loads[h])
+        where[h] = b
+    return where, bins
+
+
+def rlb_units(row_ptr: np.ndarray, nqb: int, G: int, n_bins: int = 8):
+    """Per-XCD queues: heads assigned by rlb_assign over the n_bins XCDs, each queue
+    its heads in assignment order with a head's units in id order, queues
+    concatenated.  Returns (work list, start of each queue + [total])."""
+    ngroups = -(-nqb // G)
+    _, bins = rlb_assign(head_loads(row_ptr, nqb), n_bins)
+    order, starts = [], []
+    for b in bins:
+        starts.append(len(order))
+        for h in b:
+            order.extend(range(h * ngroups, (h + 1) * ngroups))
+    starts.append(len(order))
+    return np.array(order, dtype=np.int64), np.array(starts, dtype=np.int64)
+
+
+# --------------------------------------------------------------------------
 # SASA, slack-aware sparsity augmentation ([FVAttn] SASA section).  After load
 # balancing every rank knows its own block count and the largest one (the
 # critical path); the difference is its slack.  A rank adds the highest-

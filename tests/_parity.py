@@ -13,6 +13,13 @@ BF16_MAX_ABS, BF16_MEAN_ABS = 2e-2, 2e-3
 F32_MAX_ABS = 1e-4
 
 
+def bf16_half_ulp(x):
+    """Half a unit in the last place of bfloat16 (8 significant bits) at |x|: the error that
+    rounding the exact value itself to bf16 may leave (2^(e-8) for |x| in [2^e, 2^(e+1)))."""
+    ax = np.maximum(np.abs(np.asarray(x, dtype=np.float64)), np.finfo(np.float32).tiny)
+    return np.ldexp(1.0, np.floor(np.log2(ax)).astype(np.int64) - 8)
+
+
 def classify_rows(gpu_row_ptr, gpu_col_idx, diag, p, row_offset=0):
     """Compare GPU CSR rows of one head with the oracle's routing diagnostics of that head.
     Returns dict(exact, excused_A, neartie_B, fail, fail_rows)."""
@@ -57,8 +64,13 @@ def merge(a, b):
     return out
 
 
+RECORDS: list = []   # (name, payload) of this session, printed in the pytest terminal summary
+
+
 def record(name: str, payload: dict):
-    """Append a parity record to gpurun_out/parity.jsonl (read back for the design notes)."""
+    """Append a parity record to gpurun_out/parity.jsonl (read back for the design notes) and
+    keep it for the terminal summary."""
+    RECORDS.append((name, dict(payload)))
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
     d = os.path.join(root, "gpurun_out")
     os.makedirs(d, exist_ok=True)

@@ -48,7 +48,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_strerror(L):
-    assert L.fvattn_version() == 10000
+    assert L.fvattn_version() == 10100
     for code in (OK, INVALID, UNSUPPORTED, CAPACITY, WORKSPACE, OVERFLOW, HIP, MISMATCH):
         s = L.fvattn_strerror(code).decode()
         assert s and s != "unknown error code"
@@ -124,10 +124,14 @@ def test_attn_validation(L):
     assert _attn(L, v=None) == INVALID
     assert _attn(L, N=1000) == MISMATCH                     # csr built for N=1024
     assert _attn(L, H=3) == MISMATCH
-    assert _attn(L, opts=fv._OptsC(9, 0, None, -1, 0)) == INVALID
-    assert _attn(L, opts=fv._OptsC(0, -4, None, -1, 0)) == INVALID
-    assert _attn(L, opts=fv._OptsC(0, 0, None, 7, 0)) == UNSUPPORTED          # unknown output dtype
-    assert _attn(L, dt=1, opts=fv._OptsC(0, 0, None, 0, 0)) == UNSUPPORTED  # fp32 inputs, bf16 output
+    assert _attn(L, opts=fv._OptsC(9, 0, None, 0, -1, 0)) == INVALID
+    assert _attn(L, opts=fv._OptsC(0, -4, None, 0, -1, 0)) == INVALID
+    assert _attn(L, opts=fv._OptsC(0, 0, None, 0, 7, 0)) == UNSUPPORTED          # unknown output dtype
+    assert _attn(L, dt=1, opts=fv._OptsC(0, 0, None, 0, 0, 0)) == UNSUPPORTED  # fp32 inputs, bf16 output
+    # trace capacity: 4 records per unit (bf16: units of 128 query rows = 2 query blocks of 64 -> 2 * 8 units)
+    assert _attn(L, opts=fv._OptsC(0, 0, FAKE, 4 * 16 - 1, -1, 0)) == INVALID
+    assert _attn(L, opts=fv._OptsC(0, 0, FAKE, 4 * 16 - 1, -1, 0), ws_bytes=1) == WORKSPACE  # ws checked first
+    assert _attn(L, dt=1, opts=fv._OptsC(0, 0, FAKE, 4 * 32 - 1, -1, 0)) == INVALID  # f32: one unit per row
     need = L.fvattn_attn_ws_bytes(1, 2, 1024, 64, 0, 64, 64)
     assert _attn(L, ws_bytes=need - 1) == WORKSPACE
     assert L.fvattn_sparse_attn(FAKE, FAKE, FAKE, FAKE, 1, 2, 1024, 64, 0, None, None, FAKE, 1 << 40,
@@ -137,11 +141,11 @@ def test_attn_validation(L):
 def test_plan_run_validation(L):
     c = _csr(2, 1024)
     need = L.fvattn_attn_ws_bytes(1, 2, 1024, 64, 0, 64, 64)
-    assert L.fvattn_attn_plan(FAKE, 1, 2, 1024, 64, 0, ctypes.byref(c), 5, FAKE, need, None) == INVALID
+    assert L.fvattn_attn_plan(FAKE, 1, 2, 1024, 64, 0, ctypes.byref(c), 9, FAKE, need, None) == INVALID
     assert L.fvattn_attn_plan(FAKE, 1, 2, 1024, 64, 0, ctypes.byref(c), 0, FAKE, need - 1, None) == WORKSPACE
     assert L.fvattn_attn_plan(FAKE, 1, 2, 1000, 64, 0, ctypes.byref(c), 0, FAKE, need, None) == MISMATCH
     assert L.fvattn_attn_plan(None, 1, 2, 1024, 64, 0, ctypes.byref(c), 0, FAKE, need, None) == INVALID
-    o = fv._OptsC(0, 0, None, -1, 0)
+    o = fv._OptsC(0, 0, None, 0, -1, 0)
     assert L.fvattn_attn_run(None, FAKE, FAKE, FAKE, 1, 2, 1024, 64, 0, ctypes.byref(c), ctypes.byref(o), FAKE,
                              need, None) == INVALID
     assert L.fvattn_attn_run(FAKE, FAKE, FAKE, FAKE, 1, 2, 1024, 64, 0, ctypes.byref(c), ctypes.byref(o), FAKE,
@@ -153,9 +157,20 @@ def test_plan_run_validation(L):
 
 def test_worklist_and_pool_validation(L):
     c = _csr()
-    assert L.fvattn_worklist(ctypes.byref(c), 7, FAKE, None, None) == INVALID
-    assert L.fvattn_worklist(None, 0, FAKE, None, None) == INVALID
-    assert L.fvattn_worklist(ctypes.byref(c), 0, None, None, None) == INVALID
+    need = L.fvattn_worklist_ws_bytes(2 * 16)
+    assert need >= 256 + 2 * 4 * 32 and L.fvattn_worklist_ws_bytes(0) == 0
+    assert L.fvattn_worklist(ctypes.byref(c), 7, 1, FAKE, FAKE, need, None) == INVALID
+    assert L.fvattn_worklist(None, 0, 1, FAKE, FAKE, need, None) == INVALID
+    assert L.fvattn_worklist(ctypes.byref(c), 0, 1, None, FAKE, need, None) == INVALID
+    assert L.fvattn_worklist(ctypes.byref(c), 0, 1, FAKE, None, need, None) == INVALID
+    assert L.fvattn_worklist(ctypes.byref(c), 0, 3, FAKE, FAKE, need, None) == INVALID      # G not in {1, 2, 4}
+    assert L.fvattn_worklist(ctypes.byref(c), 4, 2, FAKE, FAKE, need - 1, None) == WORKSPACE
+    big = _csr(5000, 1024)
+    assert L.fvattn_worklist(ctypes.byref(big), 4, 1, FAKE, FAKE, 1 << 40, None) == UNSUPPORTED  # > 4096 heads
+    st = ctypes.c_uint32(0)
+    assert L.fvattn_ws_status(None, 0, ctypes.byref(st), None) == INVALID
+    assert L.fvattn_ws_status(FAKE, 2, ctypes.byref(st), None) == INVALID
+    assert L.fvattn_ws_status(FAKE, 0, None, None) == INVALID
     assert L.fvattn_pool(FAKE, 2, 1024, 64, 0, 48, FAKE, None) == UNSUPPORTED
     assert L.fvattn_pool(None, 2, 1024, 64, 0, 64, FAKE, None) == INVALID
     assert L.fvattn_pool(FAKE, 2, 0, 64, 0, 64, FAKE, None) == INVALID

@@ -68,8 +68,9 @@ def test_random_shape_parity(label, args, p):
     q, k, v = workloads.make_qkv(w)
     qd, kd, vd = to_dev(q, w.dtype), to_dev(k, w.dtype), to_dev(v, w.dtype)
     # routing
-    csr_g = fv.route(qd, kd, w.block_q, w.block_k, p)
-    torch.cuda.synchronize()
+    ws = torch.empty(fv.route_ws_bytes(1, w.H, w.N, w.d, w.block_q, w.block_k), dtype=torch.uint8, device=DEV)
+    csr_g = fv.route(qd, kd, w.block_q, w.block_k, p, ws=ws)
+    assert fv.ws_status(ws, "route") == 0
     rp = csr_g.row_ptr.cpu().numpy().astype(np.int64)
     ci = csr_g.col_idx[: int(rp[-1])].cpu().numpy().astype(np.int64)
     hl = csr_g.head_load.cpu().numpy().astype(np.int64)

@@ -39,9 +39,11 @@ def to_dev(x, dtype):
 
 def gpu_sasa(qd, kd, bq, bk, p, groups, alpha, tau, critical=0, **variant):
     added = torch.zeros(groups, dtype=torch.int32, device=DEV)
+    B, H, N, d = qd.shape
+    ws = torch.empty(fv.lib().fvattn_route_sasa_ws_bytes(B, H, N, d, bq, bk, groups), dtype=torch.uint8, device=DEV)
     csr = fv.route_sasa(qd, kd, bq, bk, p, groups=groups, alpha=alpha, tau=tau, critical=critical, added=added,
-                        **variant)
-    torch.cuda.synchronize()
+                        ws=ws, **variant)
+    assert fv.ws_status(ws, "route") == 0
     rp = csr.row_ptr.cpu().numpy().astype(np.int64)
     ci = csr.col_idx[: int(rp[-1])].cpu().numpy().astype(np.int64)
     hl = csr.head_load.cpu().numpy().astype(np.int64)

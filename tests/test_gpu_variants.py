@@ -34,8 +34,10 @@ def to_dev(x, dtype):
 
 
 def gpu_route(qd, kd, bq, bk, p, **variant):
-    csr = fv.route(qd, kd, bq, bk, p, **variant)
-    torch.cuda.synchronize()
+    B, H, N, d = qd.shape
+    ws = torch.empty(fv.route_ws_bytes(B, H, N, d, bq, bk), dtype=torch.uint8, device=DEV)
+    csr = fv.route(qd, kd, bq, bk, p, ws=ws, **variant)
+    assert fv.ws_status(ws, "route") == 0
     rp = csr.row_ptr.cpu().numpy().astype(np.int64)
     ci = csr.col_idx[: int(rp[-1])].cpu().numpy().astype(np.int64)
     hl = csr.head_load.cpu().numpy().astype(np.int64)

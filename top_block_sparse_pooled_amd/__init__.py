@@ -15,14 +15,15 @@ from typing import Optional
 
 __all__ = [
     "FvAttnError", "Csr", "lib", "version", "csr_max_nnz", "route_ws_bytes", "attn_ws_bytes",
-    "pool", "route", "worklist", "sparse_attn", "attn_plan", "attn_run", "SCHED",
+    "pool", "route", "worklist", "sparse_attn", "attn_plan", "attn_run", "SCHED", "ws_status", "plan_worklist",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfvattn.so")
 
 BF16, F32 = 0, 1
-SCHED = {"lpt": 0, "identity": 1, "head_lpt": 2, "xcd": 3}
+SCHED = {"lpt": 0, "identity": 1, "head_lpt": 2, "xcd": 3, "rlb": 4, "head_desc": 5}
+STATUS = {"select_nocross": 1, "plan_mismatch": 2}
 ROUTE_MODES = {"topp": 0, "topk": 1}
 
 
@@ -41,7 +42,7 @@ class _CsrC(ctypes.Structure):
 
 class _OptsC(ctypes.Structure):
     _fields_ = [("schedule", ctypes.c_int32), ("grid", ctypes.c_int32), ("trace", ctypes.c_void_p),
-                ("out_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("trace_cap", ctypes.c_int64), ("out_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class _RouteOptsC(ctypes.Structure):
@@ -88,8 +89,12 @@ def lib() -> ctypes.CDLL:
         L.fvattn_route_sasa.restype = i32
         L.fvattn_route_sasa.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32, ctypes.POINTER(_RouteOptsC),
                                         ctypes.POINTER(_SasaOptsC), ctypes.POINTER(_CsrC), vp, sz, vp]
+        L.fvattn_worklist_ws_bytes.restype = sz
+        L.fvattn_worklist_ws_bytes.argtypes = [i32]
         L.fvattn_worklist.restype = i32
-        L.fvattn_worklist.argtypes = [ctypes.POINTER(_CsrC), i32, vp, vp, vp]
+        L.fvattn_worklist.argtypes = [ctypes.POINTER(_CsrC), i32, i32, vp, vp, sz, vp]
+        L.fvattn_ws_status.restype = i32
+        L.fvattn_ws_status.argtypes = [vp, i32, ctypes.POINTER(ctypes.c_uint32), vp]
         L.fvattn_attn_plan.restype = i32
         L.fvattn_attn_plan.argtypes = [vp, i32, i32, i32, i32, i32, ctypes.POINTER(_CsrC), i32, vp, sz, vp]
         L.fvattn_attn_run.restype = i32
@@ -283,16 +288,39 @@ def route_sasa(q, k, block_q: int, block_k: int, p: float = 0.9, groups: int = 8
     return csr
 
 
-def worklist(csr: Csr, schedule: str = "lpt", with_counter: bool = False):
-    """Device-built work list (permutation of the CSR rows) in the given order."""
+def worklist(csr: Csr, schedule: str = "lpt", G: int = 1, with_control: bool = False):
+    """Device-built work list: a permutation of the units (G adjacent query blocks of one head;
+    G = 1: CSR rows) in the given order.  with_control: also return the 64-word control block
+    (per-XCD queue starts at words 16..24)."""
     torch = _torch()
-    wl = torch.empty(csr.rows, dtype=torch.int32, device=csr.row_ptr.device)
-    ctr = torch.empty(64, dtype=torch.int32, device=wl.device) if with_counter else None
+    units = csr.bh * -(-csr.nqb // G)
+    wl = torch.empty(units, dtype=torch.int32, device=csr.row_ptr.device)
+    need = lib().fvattn_worklist_ws_bytes(csr.rows)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=wl.device)
     c = csr.c()
-    _check(lib().fvattn_worklist(ctypes.byref(c), SCHED[schedule], wl.data_ptr(),
-                                 ctr.data_ptr() if ctr is not None else None, _stream(wl.device)),
-           "fvattn_worklist")
-    return (wl, ctr) if with_counter else wl
+    _check(lib().fvattn_worklist(ctypes.byref(c), SCHED[schedule], int(G), wl.data_ptr(), ws.data_ptr(), ws.numel(),
+                                 _stream(wl.device)), "fvattn_worklist")
+    return (wl, ws[:256].view(torch.int32)) if with_control else wl
+
+
+def ws_status(ws, which: str) -> int:
+    """Status word (FVATTN_STATUS_* bits) that the last call left in a routing ("route") or
+    attention ("attn") workspace; synchronises the current stream."""
+    out = ctypes.c_uint32(0)
+    _check(lib().fvattn_ws_status(ws.data_ptr(), {"route": 0, "attn": 1}[which], ctypes.byref(out),
+                                  _stream(ws.device)), "fvattn_ws_status")
+    return int(out.value)
+
+
+def _trace_arg(trace):
+    """(pointer, capacity in uint64 elements) of an optional int64/uint64 device trace tensor."""
+    torch = _torch()
+    if trace is None:
+        return None, 0
+    if trace.dtype not in (torch.int64, getattr(torch, "uint64", torch.int64)) or not trace.is_cuda \
+            or not trace.is_contiguous():
+        raise ValueError("trace must be a contiguous int64 CUDA tensor")
+    return trace.data_ptr(), trace.numel()
 
 
 def sparse_attn(q, k, v, csr: Csr, schedule: str = "identity", grid: int = 0, trace=None, out=None, ws=None,
@@ -310,8 +338,8 @@ def sparse_attn(q, k, v, csr: Csr, schedule: str = "identity", grid: int = 0, tr
     need = attn_ws_bytes(B, H, N, d, _dtype_code(q), csr.block_q, csr.block_k)
     if ws is None:
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    opts = _OptsC(SCHED[schedule], grid, trace.data_ptr() if trace is not None else None,
-                  -1 if odt == q.dtype else _dtype_code(out), 0)
+    tp, tcap = _trace_arg(trace)
+    opts = _OptsC(SCHED[schedule], grid, tp, tcap, -1 if odt == q.dtype else _dtype_code(out), 0)
     c = csr.c()
     _check(lib().fvattn_sparse_attn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, N, d,
                                     _dtype_code(q), ctypes.byref(c), ctypes.byref(opts), ws.data_ptr(),
@@ -350,9 +378,17 @@ def attn_run(q, k, v, csr: Csr, ws, out=None, out_dtype=None, grid: int = 0, tra
     _check_qkv(q, k, v)
     B, H, N, d = q.shape
     out, odc = _attn_out(q, out, out_dtype)
-    opts = _OptsC(0, grid, trace.data_ptr() if trace is not None else None, odc, 0)
+    tp, tcap = _trace_arg(trace)
+    opts = _OptsC(0, grid, tp, tcap, odc, 0)
     c = csr.c()
     _check(lib().fvattn_attn_run(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, N, d,
                                  _dtype_code(q), ctypes.byref(c), ctypes.byref(opts), ws.data_ptr(), ws.numel(),
                                  _stream(q.device)), "fvattn_attn_run")
     return out
+
+
+def plan_worklist(csr: Csr, ws, units: int):
+    """The work list that fvattn_attn_plan left in an attention workspace (first `units`
+    entries, after the 256-byte control block)."""
+    torch = _torch()
+    return ws[256:256 + 4 * units].view(torch.int32)

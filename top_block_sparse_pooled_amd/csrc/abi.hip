@@ -8,7 +8,7 @@
 namespace fv {
 int launch_pool(const void *x, int BH, int N, int d, int dtype, int block, double *out, hipStream_t st);
 int launch_pool_k(const void *k, int BH, int N, int d, int dtype, int block_k, double *ksw, int32_t *zero0, int nzero0,
-                  int32_t *zero1, int nzero1, hipStream_t st);
+                  int32_t *zero1, int nzero1, int32_t *zero2, int nzero2, hipStream_t st);
 size_t sasa_group_bytes(int R);
 size_t sasa_hist_bytes(int R);
 int launch_sasa(const double *imp, uint32_t *bitmask, int32_t *counts, int32_t *bsum, int32_t *head_load, int nkw,
@@ -16,18 +16,19 @@ int launch_sasa(const double *imp, uint32_t *bitmask, int32_t *counts, int32_t *
                 uint32_t *ghist, int32_t *tiecnt, int32_t *tiepre, int32_t *added_out, hipStream_t st);
 int launch_select(const void *q, const double *ksw, int BH, int d, int dtype, int nqb, int nkb, double p,
                   int32_t *counts, uint32_t *bitmask, int nkw, int32_t *head_load, int32_t *bsum, int mode, int topk,
-                  int k_min, int k_max, int window, int bq, int bk, int N, double *imp, hipStream_t st);
+                  int k_min, int k_max, int window, int bq, int bk, int N, double *imp, uint32_t *status,
+                  hipStream_t st);
 int launch_csr(const int32_t *counts, const uint32_t *bitmask, const int32_t *bsum, int rows, int nkw, int nkb,
                int32_t *row_ptr, int32_t *col_idx, hipStream_t st);
-int launch_worklist(const int32_t *row_ptr, int rows, int nqb, int nkb, int G, int sched, int32_t *wl,
-                    int32_t *counter, hipStream_t st);
+int launch_plan(const int32_t *row_ptr, int rows, int nqb, int nkb, int G, int sched, int32_t *wl, int32_t *tmp,
+                int32_t *counter, const int *sig, hipStream_t st);
 int launch_attn_bf16(const void *q, const void *k, const void *v, void *o, int out_f32,
                      const int32_t *row_ptr,
-                     const int32_t *col_idx, const int32_t *wl, int32_t *counter, int rows, int nqb, int N,
+                     const int32_t *col_idx, const int32_t *wl, int32_t *counter, int rows, int nqb, int nkb, int N,
                      int D, int BQ, int BK, int grid, uint64_t *trace, hipStream_t st);
 int launch_attn_f32(const void *q, const void *k, const void *v, void *o, const int32_t *row_ptr,
-                    const int32_t *col_idx, const int32_t *wl, int rows, int nqb, int N, int D, int BQ, int BK,
-                    uint64_t *trace, hipStream_t st);
+                    const int32_t *col_idx, const int32_t *wl, int32_t *counter, int rows, int nqb, int nkb, int N,
+                    int D, int BQ, int BK, uint64_t *trace, hipStream_t st);
 }  // namespace fv
 
 namespace {
@@ -62,6 +63,7 @@ int check_shape(int B, int H, int N, int d, int bq, int bk, Shape *s) {
 }
 
 struct RouteWs {
+  uint32_t *status; // FVATTN_STATUS_* bits (first 4 bytes of the workspace)
   double *ksw;      // pooled K (the query blocks are pooled inside the select kernel)
   int32_t *counts;
   uint32_t *bitmask;
@@ -73,6 +75,8 @@ struct RouteWs {
 RouteWs route_ws_layout(const Shape &s, char *base) {
   RouteWs w;
   size_t off = 0;
+  w.status = (uint32_t *)(base + off);
+  off += 256;
   w.ksw = (double *)(base + off);
   off += align256((size_t)s.BH * s.nkbp * s.d * sizeof(double));
   w.counts = (int32_t *)(base + off);
@@ -113,19 +117,21 @@ SasaWs sasa_ws_layout(const Shape &s, int R, char *base) {
   return w;
 }
 
+// Attention workspace: the plan's control block (fv::ctl), the work list and the sort scratch.
 struct AttnWs {
-  int32_t *worklist, *counter;
+  int32_t *counter, *worklist, *tmp;
   size_t bytes;
 };
 
-AttnWs attn_ws_layout(const Shape &s, int dtype, char *base) {
+AttnWs attn_ws_layout(int rows, char *base) {
   AttnWs w;
   size_t off = 0;
-  w.worklist = (int32_t *)(base + off);
-  off += align256((size_t)s.rows * sizeof(int32_t));
   w.counter = (int32_t *)(base + off);
-  off += 256;
-  (void)dtype;
+  off += align256(fv::ctl::kWords * sizeof(int32_t));
+  w.worklist = (int32_t *)(base + off);
+  off += align256((size_t)rows * sizeof(int32_t));
+  w.tmp = (int32_t *)(base + off);
+  off += align256((size_t)rows * sizeof(int32_t));
   w.bytes = off;
   return w;
 }
@@ -168,7 +174,7 @@ size_t fvattn_route_ws_bytes(int B, int H, int N, int d, int block_q, int block_
 size_t fvattn_attn_ws_bytes(int B, int H, int N, int d, int dtype, int block_q, int block_k) {
   Shape s;
   if (!dtype_ok(dtype) || check_shape(B, H, N, d, block_q, block_k, &s) != FVATTN_OK) return 0;
-  return attn_ws_layout(s, dtype, nullptr).bytes;
+  return attn_ws_layout(s.rows, nullptr).bytes;
 }
 
 int fvattn_pool(const void *x, int BH, int N, int d, int dtype, int block, double *out, void *stream) {
@@ -204,12 +210,13 @@ int route_core(const void *q, const void *k, const Shape &s, int N, int d, int d
                hipStream_t st) {
   int rc;
   csr->bh = s.BH; csr->n = N; csr->block_q = block_q; csr->block_k = block_k; csr->nqb = s.nqb; csr->nkb = s.nkb;
-  if ((rc = fv::launch_pool_k(k, s.BH, N, d, dtype, block_k, w.ksw, w.bsum, w.nblk, csr->head_load, s.BH, st)) !=
-      FVATTN_OK)
+  if ((rc = fv::launch_pool_k(k, s.BH, N, d, dtype, block_k, w.ksw, w.bsum, w.nblk, csr->head_load, s.BH,
+                              (int32_t *)w.status, 1, st)) != FVATTN_OK)
     return rc;
   const double p = o.mode == FVATTN_ROUTE_TOPP ? o.p : 1.0;
   if ((rc = fv::launch_select(q, w.ksw, s.BH, d, dtype, s.nqb, s.nkb, p, w.counts, w.bitmask, s.nkw, csr->head_load,
-                              w.bsum, o.mode, o.topk, o.k_min, o.k_max, o.window, block_q, block_k, N, imp, st)) !=
+                              w.bsum, o.mode, o.topk, o.k_min, o.k_max, o.window, block_q, block_k, N, imp, w.status,
+                              st)) !=
       FVATTN_OK)
     return rc;
   if (!csr_after) return FVATTN_OK;
@@ -279,17 +286,46 @@ int fvattn_route(const void *q, const void *k, int B, int H, int N, int d, int d
   return fvattn_route_ex(q, k, B, H, N, d, dtype, block_q, block_k, &o, csr, ws, ws_bytes, stream);
 }
 
-int fvattn_worklist(const fvattn_csr *csr, int schedule, int32_t *worklist, int32_t *counter, void *stream) {
-  if (csr == nullptr || worklist == nullptr || csr->row_ptr == nullptr) return FVATTN_ERR_INVALID;
-  if (schedule != FVATTN_SCHED_LPT && schedule != FVATTN_SCHED_IDENTITY && schedule != FVATTN_SCHED_HEAD_LPT &&
-      schedule != FVATTN_SCHED_XCD)
-    return FVATTN_ERR_INVALID;
+size_t fvattn_worklist_ws_bytes(int rows) {
+  if (rows <= 0) return 0;
+  return attn_ws_layout(rows, nullptr).bytes;
+}
+
+namespace {
+bool sched_known(int sched) {
+  return sched == FVATTN_SCHED_LPT || sched == FVATTN_SCHED_IDENTITY || sched == FVATTN_SCHED_HEAD_LPT ||
+         sched == FVATTN_SCHED_XCD || sched == FVATTN_SCHED_RLB || sched == FVATTN_SCHED_HEAD_DESC;
+}
+bool sched_by_head(int sched) {
+  return sched == FVATTN_SCHED_HEAD_LPT || sched == FVATTN_SCHED_RLB || sched == FVATTN_SCHED_HEAD_DESC;
+}
+constexpr int kMaxPlanHeads = 4096;   // heads the head-ordered schedules rank on the device
+}  // namespace
+
+int fvattn_worklist(const fvattn_csr *csr, int schedule, int G, int32_t *worklist, void *ws, size_t ws_bytes,
+                    void *stream) {
+  if (csr == nullptr || worklist == nullptr || ws == nullptr || csr->row_ptr == nullptr) return FVATTN_ERR_INVALID;
+  if (!sched_known(schedule)) return FVATTN_ERR_INVALID;
+  if (G != 1 && G != 2 && G != 4) return FVATTN_ERR_INVALID;
   if (csr->bh <= 0 || csr->nqb <= 0 || csr->nkb <= 0) return FVATTN_ERR_INVALID;
   if (csr->nkb > kMaxNkb) return FVATTN_ERR_UNSUPPORTED;
-  if (schedule == FVATTN_SCHED_HEAD_LPT && csr->bh > 1024) return FVATTN_ERR_UNSUPPORTED;
-  if ((long long)csr->bh * csr->nqb >= (1ll << 31)) return FVATTN_ERR_OVERFLOW;
-  return fv::launch_worklist(csr->row_ptr, csr->bh * csr->nqb, csr->nqb, csr->nkb, 1, schedule, worklist, counter,
-                             (hipStream_t)stream);
+  if (sched_by_head(schedule) && csr->bh > kMaxPlanHeads) return FVATTN_ERR_UNSUPPORTED;
+  if ((long long)csr->bh * csr->nqb >= (1ll << 31) || (long long)csr->nqb * csr->nkb >= (1ll << 31))
+    return FVATTN_ERR_OVERFLOW;
+  const int rows = csr->bh * csr->nqb;
+  const AttnWs w = attn_ws_layout(rows, (char *)ws);
+  if (ws_bytes < w.bytes) return FVATTN_ERR_WORKSPACE;
+  return fv::launch_plan(csr->row_ptr, rows, csr->nqb, csr->nkb, G, schedule, worklist, w.tmp, w.counter, nullptr,
+                         (hipStream_t)stream);
+}
+
+int fvattn_ws_status(const void *ws, int which, uint32_t *status, void *stream) {
+  if (ws == nullptr || status == nullptr || (which != 0 && which != 1)) return FVATTN_ERR_INVALID;
+  const char *src = (const char *)ws + (which == 0 ? 0 : fv::ctl::kStatus * sizeof(int32_t));
+  hipStream_t st = (hipStream_t)stream;
+  if (hipMemcpyAsync(status, src, sizeof(uint32_t), hipMemcpyDeviceToHost, st) != hipSuccess) return FVATTN_ERR_HIP;
+  if (hipStreamSynchronize(st) != hipSuccess) return FVATTN_ERR_HIP;
+  return FVATTN_OK;
 }
 
 namespace {
@@ -303,45 +339,63 @@ int attn_checks(const void *v, int B, int H, int N, int d, int dtype, const fvat
   if (v == nullptr || ws == nullptr) return FVATTN_ERR_INVALID;
   if (csr->row_ptr == nullptr || csr->col_idx == nullptr) return FVATTN_ERR_INVALID;
   if (csr->bh != s->BH || csr->n != N || csr->nqb != s->nqb || csr->nkb != s->nkb) return FVATTN_ERR_MISMATCH;
-  *w = attn_ws_layout(*s, dtype, (char *)ws);
+  *w = attn_ws_layout(s->rows, (char *)ws);
   if (ws_bytes < w->bytes) return FVATTN_ERR_WORKSPACE;
   return FVATTN_OK;
 }
 
 int sched_ok(int sched, const Shape &s) {
-  if (sched != FVATTN_SCHED_LPT && sched != FVATTN_SCHED_IDENTITY && sched != FVATTN_SCHED_HEAD_LPT &&
-      sched != FVATTN_SCHED_XCD)
-    return FVATTN_ERR_INVALID;
-  if (sched == FVATTN_SCHED_HEAD_LPT && s.BH > 1024) return FVATTN_ERR_UNSUPPORTED;
+  if (!sched_known(sched)) return FVATTN_ERR_INVALID;
+  if (sched_by_head(sched) && s.BH > kMaxPlanHeads) return FVATTN_ERR_UNSUPPORTED;
   return FVATTN_OK;
 }
 
-int run_checks(const void *q, const void *k, void *o, int dtype, const fvattn_attn_opts *opts, int *grid,
-               uint64_t **trace, int *out_dt) {
+// Query blocks per work unit: the bf16 kernel's units are 128 query rows; the float32 kernel's
+// are single query blocks.
+int unit_blocks(int dtype, int block_q) { return dtype == FVATTN_BF16 ? 128 / block_q : 1; }
+
+// Signature of a plan: what the run kernels compare before consuming it.
+void plan_sig(const Shape &s, int dtype, int sig[fv::ctl::kSigLen]) {
+  const int G = unit_blocks(dtype, s.bq);
+  sig[0] = s.BH * fv::cdiv(s.nqb, G);
+  sig[1] = G;
+  sig[2] = dtype;
+  sig[3] = s.nqb;
+  sig[4] = s.BH;
+  sig[5] = s.nkb;
+  sig[6] = s.N;
+  sig[7] = fv::ctl::kMagic;
+}
+
+int run_checks(const void *q, const void *k, void *o, int dtype, const Shape &s, const fvattn_attn_opts *opts,
+               int *grid, uint64_t **trace, int *out_dt) {
   if (q == nullptr || k == nullptr || o == nullptr) return FVATTN_ERR_INVALID;
   *grid = opts ? opts->grid : 0;
   if (*grid < 0) return FVATTN_ERR_INVALID;
   *trace = opts ? opts->trace : nullptr;
+  if (*trace != nullptr) {
+    const long long units = (long long)s.BH * fv::cdiv(s.nqb, unit_blocks(dtype, s.bq));
+    if (opts->trace_cap < 4 * units) return FVATTN_ERR_INVALID;
+  }
   *out_dt = (opts && opts->out_dtype >= 0) ? opts->out_dtype : dtype;
   if (!dtype_ok(*out_dt) || (dtype == FVATTN_F32 && *out_dt != FVATTN_F32)) return FVATTN_ERR_UNSUPPORTED;
   return FVATTN_OK;
 }
 
-int do_plan(const void *v, const Shape &s, int dtype, const fvattn_csr *csr, int sched, const AttnWs &w,
-            hipStream_t st) {
-  // bf16 attention consumes units of 128 query rows (128 / block_q query blocks); fp32: rows
-  const int G = dtype == FVATTN_BF16 ? 128 / csr->block_q : 1;
-  (void)v;
-  return fv::launch_worklist(csr->row_ptr, s.rows, s.nqb, s.nkb, G, sched, w.worklist, w.counter, st);
+int do_plan(const Shape &s, int dtype, const fvattn_csr *csr, int sched, const AttnWs &w, hipStream_t st) {
+  int sig[fv::ctl::kSigLen];
+  plan_sig(s, dtype, sig);
+  return fv::launch_plan(csr->row_ptr, s.rows, s.nqb, s.nkb, sig[1], sched, w.worklist, w.tmp, w.counter, sig, st);
 }
 
 int do_run(const void *q, const void *k, const void *v, void *o, const Shape &s, int dtype, int out_dt,
            const fvattn_csr *csr, int grid, uint64_t *trace, const AttnWs &w, hipStream_t st) {
   if (dtype == FVATTN_F32)
-    return fv::launch_attn_f32(q, k, v, o, csr->row_ptr, csr->col_idx, w.worklist, s.rows, s.nqb, s.N, s.d,
-                               csr->block_q, csr->block_k, trace, st);
+    return fv::launch_attn_f32(q, k, v, o, csr->row_ptr, csr->col_idx, w.worklist, w.counter, s.rows, s.nqb, s.nkb,
+                               s.N, s.d, csr->block_q, csr->block_k, trace, st);
   return fv::launch_attn_bf16(q, k, v, o, out_dt == FVATTN_F32, csr->row_ptr, csr->col_idx, w.worklist,
-                              w.counter, s.rows, s.nqb, s.N, s.d, csr->block_q, csr->block_k, grid, trace, st);
+                              w.counter, s.rows, s.nqb, s.nkb, s.N, s.d, csr->block_q, csr->block_k, grid, trace,
+                              st);
 }
 }  // namespace
 
@@ -352,7 +406,7 @@ int fvattn_attn_plan(const void *v, int B, int H, int N, int d, int dtype, const
   int rc = attn_checks(v, B, H, N, d, dtype, csr, &s, ws, ws_bytes, &w);
   if (rc != FVATTN_OK) return rc;
   if ((rc = sched_ok(schedule, s)) != FVATTN_OK) return rc;
-  return do_plan(v, s, dtype, csr, schedule, w, (hipStream_t)stream);
+  return do_plan(s, dtype, csr, schedule, w, (hipStream_t)stream);
 }
 
 int fvattn_attn_run(const void *q, const void *k, const void *v, void *o, int B, int H, int N, int d, int dtype,
@@ -363,7 +417,7 @@ int fvattn_attn_run(const void *q, const void *k, const void *v, void *o, int B,
   if (rc != FVATTN_OK) return rc;
   int grid, out_dt;
   uint64_t *trace;
-  if ((rc = run_checks(q, k, o, dtype, opts, &grid, &trace, &out_dt)) != FVATTN_OK) return rc;
+  if ((rc = run_checks(q, k, o, dtype, s, opts, &grid, &trace, &out_dt)) != FVATTN_OK) return rc;
   return do_run(q, k, v, o, s, dtype, out_dt, csr, grid, trace, w, (hipStream_t)stream);
 }
 
@@ -378,9 +432,9 @@ int fvattn_sparse_attn(const void *q, const void *k, const void *v, void *o, int
   if ((rc = sched_ok(sched, s)) != FVATTN_OK) return rc;
   int grid, out_dt;
   uint64_t *trace;
-  if ((rc = run_checks(q, k, o, dtype, opts, &grid, &trace, &out_dt)) != FVATTN_OK) return rc;
+  if ((rc = run_checks(q, k, o, dtype, s, opts, &grid, &trace, &out_dt)) != FVATTN_OK) return rc;
   hipStream_t st = (hipStream_t)stream;
-  if ((rc = do_plan(v, s, dtype, csr, sched, w, st)) != FVATTN_OK) return rc;
+  if ((rc = do_plan(s, dtype, csr, sched, w, st)) != FVATTN_OK) return rc;
   return do_run(q, k, v, o, s, dtype, out_dt, csr, grid, trace, w, st);
 }
 

@@ -27,174 +27,6 @@
 namespace fv {
 
 // ---------------------------------------------------------------------------------------
-// k_worklist: permutation of the work units in the requested order.  A unit is G consecutive
-// query blocks of one head (G = 1: a CSR row); unit u = bh * ngroups + g covers rows
-// bh*nqb + g*G .. min(bh*nqb + g*G + G, (bh+1)*nqb) - 1, so its work (kept blocks) is one
-// difference of row_ptr.  Single workgroup of 1024 threads (16 waves).
-//   LPT:      key = nkb - ceil(work / G) (ascending key = heaviest first), stable in unit id.
-//   HEAD_LPT: heads by load descending (ties: head id), then each head's units as LPT.
-//   IDENTITY: unit id order.  XCD: unit id order cut into 8 ranges of equal work.
-// Stable counting sort: per-wave bin counts in LDS, bases by scan, then each wave scatters
-// its units in 64-unit chunks, ranking equal keys inside a chunk with bit-sliced ballots.
-// ---------------------------------------------------------------------------------------
-constexpr int kWlWaves = 16;
-constexpr int kWlMaxBins = 1281 + 3;
-
-struct UnitMap {
-  const int32_t *row_ptr;
-  int nqb, G, ngroups, nkb;
-  __device__ __forceinline__ int first_row(int u) const {
-    const int bh = u / ngroups, g = u - bh * ngroups;
-    return bh * nqb + g * G;
-  }
-  __device__ __forceinline__ int work(int u) const {
-    const int bh = u / ngroups, g = u - bh * ngroups;
-    const int r0 = bh * nqb + g * G, r1 = min(r0 + G, (bh + 1) * nqb);
-    return row_ptr[r1] - row_ptr[r0];
-  }
-  __device__ __forceinline__ int key(int u) const {
-    int c = (work(u) + G - 1) / G;
-    c = c < 0 ? 0 : (c > nkb ? nkb : c);
-    return nkb - c;
-  }
-};
-
-// Stable scatter of units [lo, hi) of one wave by key, into out[] at positions given by the
-// running per-key bases in bins[] (already offset).  Keys < 2048.
-__device__ void wl_scatter(const UnitMap &um, int lo, int hi, int *bins, int32_t *out) {
-  const int lane = threadIdx.x & 63;
-  const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int c0 = lo; c0 < hi; c0 += 64) {
-    const int u = c0 + lane;
-    const bool act = u < hi;
-    const int key = act ? um.key(u) : 0;
-    unsigned long long peers = __ballot(act);
-#pragma unroll
-    for (int b = 0; b < 11; ++b) {
-      const unsigned long long bb = __ballot(act && ((key >> b) & 1));
-      peers &= ((key >> b) & 1) ? bb : ~bb;
-    }
-    const int rank = __popcll(peers & lt);
-    int base = 0;
-    if (act) base = bins[key];
-    __builtin_amdgcn_s_waitcnt(0);
-    __builtin_amdgcn_wave_barrier();
-    if (act) {
-      out[base + rank] = u;
-      if (rank == 0) bins[key] = base + __popcll(peers);
-    }
-    __builtin_amdgcn_wave_barrier();
-  }
-}
-
-__global__ __launch_bounds__(1024) void k_worklist(const int32_t *__restrict__ row_ptr, int rows, int nqb,
-                                                   int nkb, int G, int sched, int32_t *__restrict__ wl,
-                                                   int32_t *__restrict__ counter) {
-  __shared__ int bins[kWlWaves][kWlMaxBins];
-  __shared__ int s_scan[1024];
-  __shared__ int s_hbase[1024];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int nh = rows / nqb;
-  const int ngroups = (nqb + G - 1) / G;
-  const int units = nh * ngroups;
-  const UnitMap um{row_ptr, nqb, G, ngroups, nkb};
-  // control block: [0] ticket, [1] exit count, [2] per-XCD mode, [8+x] XCD x ticket,
-  // [16+x] start of XCD x's unit range (x = 0..8, [24] = units)
-  if (tid == 0 && counter != nullptr) {
-    counter[0] = 0;
-    counter[1] = 0;
-    counter[2] = (sched == FVATTN_SCHED_XCD) ? 1 : 0;
-  }
-  if (sched == FVATTN_SCHED_IDENTITY || sched == FVATTN_SCHED_XCD) {
-    for (int u = tid; u < units; u += 1024) wl[u] = u;
-    if (sched == FVATTN_SCHED_XCD && counter != nullptr && tid < 9) {
-      // range x starts at the first unit whose kept blocks begin at or after x/8 of the total
-      const long long nnz = row_ptr[rows];
-      const long long target = nnz * tid / 8;
-      int lo = 0, hi = units;   // first unit u with row_ptr[first_row(u)] >= target
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (row_ptr[um.first_row(mid)] < target) lo = mid + 1; else hi = mid;
-      }
-      const int start = tid == 8 ? units : lo;
-      counter[16 + tid] = start;
-      if (tid < 8) counter[8 + tid] = start;
-    }
-    return;
-  }
-  const int nbins = nkb + 1;
-  if (sched == FVATTN_SCHED_LPT) {
-    for (int i = tid; i < kWlWaves * kWlMaxBins; i += 1024) (&bins[0][0])[i] = 0;
-    __syncthreads();
-    const int seg = cdiv(units, kWlWaves);
-    const int lo = min(units, w * seg), hi = min(units, lo + seg);
-    for (int u = lo + lane; u < hi; u += 64) atomicAdd(&bins[w][um.key(u)], 1);
-    __syncthreads();
-    // totals per bin, exclusive scan over bins (two bins per thread)
-    int t0 = 0, t1 = 0;
-    const int b0 = 2 * tid, b1 = 2 * tid + 1;
-    for (int i = 0; i < kWlWaves; ++i) {
-      if (b0 < nbins) t0 += bins[i][b0];
-      if (b1 < nbins) t1 += bins[i][b1];
-    }
-    s_scan[tid] = t0 + t1;
-    __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-      const int o = tid >= off ? s_scan[tid - off] : 0;
-      __syncthreads();
-      s_scan[tid] += o;
-      __syncthreads();
-    }
-    int run0 = s_scan[tid] - (t0 + t1);
-    int run1 = run0 + t0;
-    for (int i = 0; i < kWlWaves; ++i) {
-      if (b0 < nbins) { const int c = bins[i][b0]; bins[i][b0] = run0; run0 += c; }
-      if (b1 < nbins) { const int c = bins[i][b1]; bins[i][b1] = run1; run1 += c; }
-    }
-    __syncthreads();
-    wl_scatter(um, lo, hi, bins[w], wl);
-    return;
-  }
-  // HEAD_LPT: rank heads by load (desc), ties by id; a head's units start at rank * ngroups
-  for (int h = tid; h < nh; h += 1024) {
-    const int lh = row_ptr[(h + 1) * nqb] - row_ptr[h * nqb];
-    int rank = 0;
-    for (int h2 = 0; h2 < nh; ++h2) {
-      const int l2 = row_ptr[(h2 + 1) * nqb] - row_ptr[h2 * nqb];
-      rank += (l2 > lh) || (l2 == lh && h2 < h);
-    }
-    s_hbase[h] = rank * ngroups;
-  }
-  __syncthreads();
-  for (int h = w; h < nh; h += kWlWaves) {
-    int *bw = bins[w];
-    for (int i = lane; i < nbins; i += 64) bw[i] = 0;
-    __builtin_amdgcn_wave_barrier();
-    const int lo = h * ngroups, hi = lo + ngroups;
-    for (int u = lo + lane; u < hi; u += 64) atomicAdd(&bw[um.key(u)], 1);
-    __builtin_amdgcn_s_waitcnt(0);
-    __builtin_amdgcn_wave_barrier();
-    // exclusive scan of the bins by this wave (chunks of 64)
-    int run = s_hbase[h];
-    for (int c0 = 0; c0 < nbins; c0 += 64) {
-      const int i = c0 + lane;
-      const int c = i < nbins ? bw[i] : 0;
-      int incl = c;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int o = __shfl_up(incl, off);
-        if (lane >= off) incl += o;
-      }
-      if (i < nbins) bw[i] = run + incl - c;
-      run += __shfl(incl, 63);
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __builtin_amdgcn_wave_barrier();
-    wl_scatter(um, lo, hi, bw, wl);
-  }
-}
-
-// ---------------------------------------------------------------------------------------
 // Geometry of a K or V tile of BK keys x D dims in LDS, loaded by NW waves as 1 KB pieces
 // straight from global memory (buffer_load ... lds; per-head buffer resources make rows past N
 // read as zero).  Rows are runs of 16-byte chunks in XOR-swizzled order (rows that share a
@@ -287,8 +119,8 @@ template <int BQ, int BK, int D>
 __global__ __launch_bounds__(512, 1) void k_attn_pp(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     void *__restrict__ o, int out_f32, const int32_t *__restrict__ row_ptr, const int32_t *__restrict__ col_idx,
-    const int32_t *__restrict__ worklist, int32_t *__restrict__ counter, int units, int ngroups, int nqb, int N,
-    float sl2, uint64_t *__restrict__ trace) {
+    const int32_t *__restrict__ worklist, int32_t *__restrict__ counter, int units, int ngroups, int nqb, int nkb,
+    int N, float sl2, uint64_t *__restrict__ trace) {
   using C = AttnCfg<64, D>;        // tile geometry (64 keys); the 4 waves of a group load its tiles
   static_assert(BK == 64 || BK == 32, "64-key tiles of one or two key blocks");
   constexpr int PB = 64 / BK;     // key blocks per tile
@@ -341,18 +173,28 @@ __global__ __launch_bounds__(512, 1) void k_attn_pp(
     tr_off[m] = (uint32_t)((4 * h + (tra >> 2)) * C::KROW + (4 * (m ^ tr_sw) + 2 * trg + ((tra & 3) >> 1)) * 16 +
                            8 * (tra & 1));
 
-  const bool per_xcd = counter[2] != 0;
+  {
+    // consume only a plan built for this launch (same dtype, unit size and CSR shape)
+    const int32_t *sg = counter + ctl::kSig;
+    const bool ok = sg[0] == units && sg[1] == G && sg[2] == FVATTN_BF16 && sg[3] == nqb && sg[4] == units / ngroups &&
+                    sg[5] == nkb && sg[6] == N && sg[7] == ctl::kMagic;
+    if (!ok) {
+      if (tid == 0) atomicOr(reinterpret_cast<uint32_t *>(counter + ctl::kStatus), (uint32_t)FVATTN_STATUS_PLAN_MISMATCH);
+      return;
+    }
+  }
+  const bool per_xcd = counter[ctl::kPerXcd] != 0;
   const int xcc = (int)(__builtin_amdgcn_s_getreg((31 << 11) | 20) & 7);   // XCC_ID
   for (;;) {
     if (tid == 0) {
       int tk = units;
       if (!per_xcd) {
-        tk = atomicAdd(&counter[0], 1);
+        tk = atomicAdd(&counter[ctl::kTicket], 1);
       } else {
         for (int qq = 0; qq < 8; ++qq) {
           const int x = (xcc + qq) & 7;
-          const int c = atomicAdd(&counter[8 + x], 1);
-          if (c < counter[17 + x]) {
+          const int c = atomicAdd(&counter[ctl::kXcdTicket + x], 1);
+          if (c < counter[ctl::kXcdStart + 1 + x]) {
             tk = c;
             break;
           }
@@ -754,10 +596,10 @@ __global__ __launch_bounds__(512, 1) void k_attn_pp(
   // The last workgroup to leave restores the ticket counters and the exit count.
   if (tid == 0) {
     __threadfence();
-    if (atomicAdd(&counter[1], 1) == (int)gridDim.x - 1) {
-      atomicExch(&counter[0], 0);
-      for (int x = 0; x < 8; ++x) atomicExch(&counter[8 + x], counter[16 + x]);
-      atomicExch(&counter[1], 0);
+    if (atomicAdd(&counter[ctl::kExit], 1) == (int)gridDim.x - 1) {
+      atomicExch(&counter[ctl::kTicket], 0);
+      for (int x = 0; x < 8; ++x) atomicExch(&counter[ctl::kXcdTicket + x], counter[ctl::kXcdStart + x]);
+      atomicExch(&counter[ctl::kExit], 0);
     }
   }
 }
@@ -771,12 +613,23 @@ __global__ __launch_bounds__(BQ) void k_attn_f32(const float *__restrict__ q, co
                                                  const float *__restrict__ v, float *__restrict__ o,
                                                  const int32_t *__restrict__ row_ptr,
                                                  const int32_t *__restrict__ col_idx,
-                                                 const int32_t *__restrict__ worklist, int nqb, int N,
+                                                 const int32_t *__restrict__ worklist,
+                                                 int32_t *__restrict__ counter, int rows, int nqb, int nkb, int N,
                                                  float scale, uint64_t *__restrict__ trace) {
   __shared__ float Kt[BK][D + 1];
   __shared__ float Vt[BK][D];
   const int tid = threadIdx.x;
   const int t = blockIdx.x;
+  {
+    // consume only a plan built for this launch (float32, one query block per unit, same CSR shape)
+    const int32_t *sg = counter + ctl::kSig;
+    const bool ok = sg[0] == rows && sg[1] == 1 && sg[2] == FVATTN_F32 && sg[3] == nqb && sg[4] == rows / nqb &&
+                    sg[5] == nkb && sg[6] == N && sg[7] == ctl::kMagic;
+    if (!ok) {
+      if (tid == 0) atomicOr(reinterpret_cast<uint32_t *>(counter + ctl::kStatus), (uint32_t)FVATTN_STATUS_PLAN_MISMATCH);
+      return;
+    }
+  }
   uint64_t t_start = 0;
   if (trace != nullptr) t_start = __builtin_amdgcn_s_memrealtime();
   const int row = worklist[t];
@@ -835,17 +688,10 @@ __global__ __launch_bounds__(BQ) void k_attn_f32(const float *__restrict__ q, co
 // ---------------------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------------------
-int launch_worklist(const int32_t *row_ptr, int rows, int nqb, int nkb, int G, int sched, int32_t *wl,
-                    int32_t *counter, hipStream_t st) {
-  hipLaunchKernelGGL(k_worklist, dim3(1), dim3(1024), 0, st, row_ptr, rows, nqb, nkb, G, sched, wl, counter);
-  FV_CHECK_LAUNCH();
-  return FVATTN_OK;
-}
-
 template <int BQ, int BK, int D>
 static int launch_attn_bf16_t(const void *q, const void *k, const void *v, void *o, int out_f32,
                               const int32_t *row_ptr, const int32_t *col_idx, const int32_t *wl, int32_t *counter,
-                              int rows, int nqb, int N, int grid, uint64_t *trace, hipStream_t st) {
+                              int rows, int nqb, int nkb, int N, int grid, uint64_t *trace, hipStream_t st) {
   // two wave groups per unit (k_attn_pp), V as given
   auto kern = k_attn_pp<BQ, BK, D>;
   const int nthreads = 512;
@@ -862,18 +708,18 @@ static int launch_attn_bf16_t(const void *q, const void *k, const void *v, void 
   const float sl2 = (float)(1.4426950408889634 / sqrt((double)D));
   hipLaunchKernelGGL(kern, dim3(grid), dim3(nthreads), 0, st, (const uint16_t *)q, (const uint16_t *)k,
                      (const uint16_t *)v, o, out_f32, row_ptr, col_idx, wl, counter, units, ngroups,
-                     nqb, N, sl2, trace);
+                     nqb, nkb, N, sl2, trace);
   FV_CHECK_LAUNCH();
   return FVATTN_OK;
 }
 
 int launch_attn_bf16(const void *q, const void *k, const void *v, void *o, int out_f32,
                      const int32_t *row_ptr,
-                     const int32_t *col_idx, const int32_t *wl, int32_t *counter, int rows, int nqb, int N,
+                     const int32_t *col_idx, const int32_t *wl, int32_t *counter, int rows, int nqb, int nkb, int N,
                      int D, int BQ, int BK, int grid, uint64_t *trace, hipStream_t st) {
 #define FV_A(bq, bk, dd)                                                                                 \
   if (BQ == bq && BK == bk && D == dd)                                                                   \
-    return launch_attn_bf16_t<bq, bk, dd>(q, k, v, o, out_f32, row_ptr, col_idx, wl, counter, rows, nqb, N, \
+    return launch_attn_bf16_t<bq, bk, dd>(q, k, v, o, out_f32, row_ptr, col_idx, wl, counter, rows, nqb, nkb, N, \
                                           grid, trace, st);
   FV_A(64, 64, 128) FV_A(128, 64, 128) FV_A(32, 64, 128) FV_A(64, 32, 128) FV_A(128, 32, 128) FV_A(32, 32, 128)
   FV_A(64, 64, 64) FV_A(128, 64, 64) FV_A(32, 64, 64) FV_A(64, 32, 64) FV_A(128, 32, 64) FV_A(32, 32, 64)
@@ -883,21 +729,21 @@ int launch_attn_bf16(const void *q, const void *k, const void *v, void *o, int o
 
 template <int BQ, int BK, int D>
 static int launch_attn_f32_t(const void *q, const void *k, const void *v, void *o, const int32_t *row_ptr,
-                             const int32_t *col_idx, const int32_t *wl, int rows, int nqb, int N, uint64_t *trace,
-                             hipStream_t st) {
+                             const int32_t *col_idx, const int32_t *wl, int32_t *counter, int rows, int nqb, int nkb,
+                             int N, uint64_t *trace, hipStream_t st) {
   const float scale = (float)(1.0 / sqrt((double)D));
   hipLaunchKernelGGL((k_attn_f32<BQ, BK, D>), dim3(rows), dim3(BQ), 0, st, (const float *)q, (const float *)k,
-                     (const float *)v, (float *)o, row_ptr, col_idx, wl, nqb, N, scale, trace);
+                     (const float *)v, (float *)o, row_ptr, col_idx, wl, counter, rows, nqb, nkb, N, scale, trace);
   FV_CHECK_LAUNCH();
   return FVATTN_OK;
 }
 
 int launch_attn_f32(const void *q, const void *k, const void *v, void *o, const int32_t *row_ptr,
-                    const int32_t *col_idx, const int32_t *wl, int rows, int nqb, int N, int D, int BQ, int BK,
-                    uint64_t *trace, hipStream_t st) {
+                    const int32_t *col_idx, const int32_t *wl, int32_t *counter, int rows, int nqb, int nkb, int N,
+                    int D, int BQ, int BK, uint64_t *trace, hipStream_t st) {
 #define FV_F(bq, bk, dd) \
   if (BQ == bq && BK == bk && D == dd) \
-    return launch_attn_f32_t<bq, bk, dd>(q, k, v, o, row_ptr, col_idx, wl, rows, nqb, N, trace, st);
+    return launch_attn_f32_t<bq, bk, dd>(q, k, v, o, row_ptr, col_idx, wl, counter, rows, nqb, nkb, N, trace, st);
   FV_F(64, 64, 128) FV_F(128, 64, 128) FV_F(32, 64, 128) FV_F(64, 32, 128) FV_F(128, 32, 128) FV_F(32, 32, 128)
   FV_F(64, 64, 64) FV_F(128, 64, 64) FV_F(32, 64, 64) FV_F(64, 32, 64) FV_F(128, 32, 64) FV_F(32, 32, 64)
 #undef FV_F

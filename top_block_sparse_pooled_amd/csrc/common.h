@@ -50,6 +50,20 @@ __device__ __forceinline__ void unpack16(const u32x4 &c, float *out, float) {
 
 __host__ __device__ constexpr inline int cdiv(int a, int b) { return (a + b - 1) / b; }
 
+// Control block of an attention plan: int32[64] at the start of the attention workspace.
+namespace ctl {
+constexpr int kTicket = 0;      // next unit of the single queue
+constexpr int kExit = 1;        // workgroups that have left (the last one restores the tickets)
+constexpr int kPerXcd = 2;      // 1: per-XCD queues with stealing
+constexpr int kXcdTicket = 8;   // [8]: next unit of XCD x's queue
+constexpr int kXcdStart = 16;   // [9]: first unit of XCD x's queue; [16 + 8] = units
+constexpr int kSig = 32;        // plan signature: units, G, dtype, nqb, bh, nkb, n, magic
+constexpr int kSigLen = 8;
+constexpr int kStatus = 40;     // FVATTN_STATUS_* bits set by the attention kernels
+constexpr int kMagic = 0x46565032;
+constexpr int kWords = 64;
+}  // namespace ctl
+
 // Smallest shift with (width - 1) >> shift < 256: the 8-bit radix digit of a key in a range of
 // `width` keys (radix selects over float64 bit patterns).
 __device__ __forceinline__ int digit_shift(unsigned long long width) {

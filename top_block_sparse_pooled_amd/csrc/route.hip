@@ -48,8 +48,8 @@ struct PoolArgs {
   double *out[2];
   int block[2], nb[2], ngrp[2];   // ngrp = ceil(nb / 16); ngrp[1] = 0 for one tensor
   int N, layout;
-  int32_t *zero[2];               // zeroed by workgroup (0, 0) (may be null)
-  int nzero[2];
+  int32_t *zero[3];               // zeroed by workgroup (0, 0) (may be null)
+  int nzero[3];
 };
 
 // Means of the real tokens of NBK blocks j0, j0 + js, ... (block j: tokens [j block,
@@ -121,7 +121,7 @@ __global__ __launch_bounds__(256) void k_pool(PoolArgs a) {
   const int t = gx < a.ngrp[0] ? 0 : 1;
   if (t) gx -= a.ngrp[0];
   if (blockIdx.x == 0 && bh == 0) {
-    for (int z = 0; z < 2; ++z)
+    for (int z = 0; z < 3; ++z)
       if (a.zero[z] != nullptr)
         for (int i = tid; i < a.nzero[z]; i += 256) a.zero[z][i] = 0;
   }
@@ -189,7 +189,7 @@ template <int NPL>
 __device__ __forceinline__ uint32_t select_row(const double (&ev)[NPL], int nkb, bool bycnt, unsigned long long T,
                                                unsigned long long lo0, bool keep_all,
                                                unsigned long long *__restrict__ hm, uint32_t *__restrict__ hc,
-                                               int &count) {
+                                               uint32_t *__restrict__ status, int &count) {
   const int lane = threadIdx.x & 63;
   unsigned long long lo = lo0;
   unsigned long long width = (unsigned long long)__double_as_longlong(1.0) + 1ull - lo0;
@@ -246,7 +246,8 @@ __device__ __forceinline__ uint32_t select_row(const double (&ev)[NPL], int nkb,
       acc += m4[q];
     }
     const unsigned long long bal = __ballot(dig >= 0);
-    if (bal == 0ull) {   // unreachable: the range always holds the crossing
+    if (bal == 0ull) {   // not expected: the range always holds the crossing.  Flag it and keep the row whole
+      if (lane == 0) atomicOr(status, (uint32_t)FVATTN_STATUS_SELECT_NOCROSS);
       st = 3;
       break;
     }
@@ -297,7 +298,7 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 ? 2 : 1) void k_select(const voi
                                                 double scale, double p, int32_t *__restrict__ counts,
                                                 uint32_t *__restrict__ bitmask, int nkw,
                                                 int32_t *__restrict__ head_load, int32_t *__restrict__ bsum,
-                                                int BH, SelOpts sel) {
+                                                int BH, SelOpts sel, uint32_t *__restrict__ status) {
   constexpr int KS = D / 4;               // MFMA k-steps
   constexpr int KCAP = 16 * NWV * MAXT;   // key blocks the tiles cover
   constexpr int NPL = KCAP / 64;          // values per lane in the row phase
@@ -496,13 +497,15 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 ? 2 : 1) void k_select(const voi
       }
       int c;
       // lane L < nkw holds kept word L (key blocks 32 L .. 32 L + 31)
-      uint32_t word = select_row<NPL>(ev, nkb, bycnt, tgt0, lo0, all, h_mass[w], h_cnt[w], c);
+      uint32_t word = select_row<NPL>(ev, nkb, bycnt, tgt0, lo0, all, h_mass[w], h_cnt[w], status, c);
       if (EXT && !bycnt && (sel.k_min > 1 || sel.k_max > 0)) {
         // clamp of the Top-p count: re-select by count when it lies outside [k_min, k_max]
         int tgt = max(c, sel.k_min);
         if (sel.k_max > 0) tgt = min(tgt, sel.k_max);
         tgt = min(tgt, nkb);
-        if (tgt != c) word = select_row<NPL>(ev, nkb, true, (unsigned long long)tgt, lo0, tgt >= nkb, h_mass[w], h_cnt[w], c);
+        if (tgt != c)
+          word = select_row<NPL>(ev, nkb, true, (unsigned long long)tgt, lo0, tgt >= nkb, h_mass[w], h_cnt[w], status,
+                                 c);
       }
       if (EXT && sel.window > 0 && lane < nkw) {
         // local window: key blocks within `window` of those overlapping the query block's tokens
@@ -642,7 +645,7 @@ int launch_pool(const void *x, int BH, int N, int d, int dtype, int block, doubl
 // Pooled K in the float64 MFMA operand order of k_select (the query blocks are pooled inside
 // k_select), and the zeroing of the two counter arrays (per-64-row sums, head loads).
 int launch_pool_k(const void *k, int BH, int N, int d, int dtype, int block_k, double *ksw, int32_t *zero0, int nzero0,
-                  int32_t *zero1, int nzero1, hipStream_t st) {
+                  int32_t *zero1, int nzero1, int32_t *zero2, int nzero2, hipStream_t st) {
   PoolArgs pa = {};
   pa.x[0] = k;
   pa.out[0] = ksw;
@@ -655,13 +658,15 @@ int launch_pool_k(const void *k, int BH, int N, int d, int dtype, int block_k, d
   pa.nzero[0] = nzero0;
   pa.zero[1] = zero1;
   pa.nzero[1] = nzero1;
+  pa.zero[2] = zero2;
+  pa.nzero[2] = nzero2;
   return launch_pool_args(pa, BH, d, dtype, st);
 }
 
 template <typename T, int D, int MT, int NWV>
 static int launch_select_mt(const void *q, const double *ksw, int BH, int nqb, int nkb, double p, int32_t *counts,
                             uint32_t *bitmask, int nkw, int32_t *head_load, int32_t *bsum, const SelOpts &sel,
-                            hipStream_t st) {
+                            uint32_t *status, hipStream_t st) {
   auto kern = (sel.mode != FVATTN_ROUTE_TOPP || sel.k_min > 1 || sel.k_max > 0 || sel.window > 0 ||
                sel.imp != nullptr)
                   ? k_select<T, D, MT, NWV, true>
@@ -675,7 +680,7 @@ static int launch_select_mt(const void *q, const double *ksw, int BH, int nqb, i
   if (grid < 8) grid = 8;   // every XCD range needs a worker
   const double scale = 1.0 / sqrt((double)D);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * NWV), 0, st, q, ksw, nqb, nkb, scale, p, counts, bitmask, nkw,
-                     head_load, bsum, BH, sel);
+                     head_load, bsum, BH, sel, status);
   FV_CHECK_LAUNCH();
   return FVATTN_OK;
 }
@@ -685,10 +690,11 @@ static int launch_select_mt(const void *q, const double *ksw, int BH, int nqb, i
 template <typename T, int D>
 static int launch_select_d(const void *q, const double *ksw, int BH, int nqb, int nkb, double p, int32_t *counts,
                            uint32_t *bitmask, int nkw, int32_t *head_load, int32_t *bsum, const SelOpts &sel,
-                           hipStream_t st) {
+                           uint32_t *status, hipStream_t st) {
   const int nkt = cdiv(nkb, 16);
 #define FV_SEL(MT, NWV) \
-  return launch_select_mt<T, D, MT, NWV>(q, ksw, BH, nqb, nkb, p, counts, bitmask, nkw, head_load, bsum, sel, st)
+  return launch_select_mt<T, D, MT, NWV>(q, ksw, BH, nqb, nkb, p, counts, bitmask, nkw, head_load, bsum, sel, status, \
+                                         st)
   if (nkt <= 4) FV_SEL(1, 4);
   if (nkt <= 8) FV_SEL(2, 4);
   if (nkt <= 16) FV_SEL(4, 4);
@@ -700,16 +706,17 @@ static int launch_select_d(const void *q, const double *ksw, int BH, int nqb, in
 
 int launch_select(const void *q, const double *ksw, int BH, int d, int dtype, int nqb, int nkb, double p,
                   int32_t *counts, uint32_t *bitmask, int nkw, int32_t *head_load, int32_t *bsum, int mode, int topk,
-                  int k_min, int k_max, int window, int bq, int bk, int N, double *imp, hipStream_t st) {
+                  int k_min, int k_max, int window, int bq, int bk, int N, double *imp, uint32_t *status,
+                  hipStream_t st) {
   const SelOpts sel{mode, topk, k_min, k_max, window, bq, bk, N, imp};
   if (dtype == FVATTN_BF16) {
     if (d == 128)
-      return launch_select_d<uint16_t, 128>(q, ksw, BH, nqb, nkb, p, counts, bitmask, nkw, head_load, bsum, sel, st);
-    return launch_select_d<uint16_t, 64>(q, ksw, BH, nqb, nkb, p, counts, bitmask, nkw, head_load, bsum, sel, st);
+      return launch_select_d<uint16_t, 128>(q, ksw, BH, nqb, nkb, p, counts, bitmask, nkw, head_load, bsum, sel, status, st);
+    return launch_select_d<uint16_t, 64>(q, ksw, BH, nqb, nkb, p, counts, bitmask, nkw, head_load, bsum, sel, status, st);
   }
   if (d == 128)
-    return launch_select_d<float, 128>(q, ksw, BH, nqb, nkb, p, counts, bitmask, nkw, head_load, bsum, sel, st);
-  return launch_select_d<float, 64>(q, ksw, BH, nqb, nkb, p, counts, bitmask, nkw, head_load, bsum, sel, st);
+    return launch_select_d<float, 128>(q, ksw, BH, nqb, nkb, p, counts, bitmask, nkw, head_load, bsum, sel, status, st);
+  return launch_select_d<float, 64>(q, ksw, BH, nqb, nkb, p, counts, bitmask, nkw, head_load, bsum, sel, status, st);
 }
 
 int launch_csr(const int32_t *counts, const uint32_t *bitmask, const int32_t *bsum, int rows, int nkw, int nkb,
