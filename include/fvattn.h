@@ -48,7 +48,9 @@ enum {
   FVATTN_ERR_WORKSPACE = -4,   /* ws_bytes smaller than the matching *_ws_bytes() size        */
   FVATTN_ERR_OVERFLOW = -5,    /* B*H*nqb*nkb does not fit in int32                            */
   FVATTN_ERR_HIP = -6,         /* a HIP launch failed                                         */
-  FVATTN_ERR_MISMATCH = -7     /* CSR shape fields do not match the attention arguments       */
+  FVATTN_ERR_MISMATCH = -7,    /* CSR shape fields do not match the attention arguments       */
+  FVATTN_ERR_SCRATCH = -8      /* problem larger than the static scratch of the no-allocation
+                                  entry point (see fvattn_sparse_attn_noalloc)                 */
 };
 
 /*
@@ -315,6 +317,21 @@ int fvattn_attn_plan(const void *v, int B, int H, int N, int d, int dtype, const
 int fvattn_attn_run(const void *q, const void *k, const void *v, void *o, int B, int H, int N,
                     int d, int dtype, const fvattn_csr *csr, const fvattn_attn_opts *opts,
                     void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * fvattn_sparse_attn without a workspace, for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  The plan
+ * (control block, work list and sort scratch) lives in a static device array sized for
+ * FVATTN_NOALLOC_MAX_ROWS rows (2 MiB), which the library holds on each GPU it runs on until the
+ * process ends; B*H*ceil(N/block_q) > FVATTN_NOALLOC_MAX_ROWS returns FVATTN_ERR_SCRATCH before
+ * anything is enqueued.  The device current on the calling thread must be the device of `stream`.
+ * Every call on one GPU shares that GPU's array, which keeps the last call's plan: calls that
+ * overlap on one GPU (several streams or host threads) race and must be serialised by the caller.
+ * Calls no allocating routine.  Arguments, outputs and errors otherwise as fvattn_sparse_attn.
+ */
+#define FVATTN_NOALLOC_MAX_ROWS 262144
+int fvattn_sparse_attn_noalloc(const void *q, const void *k, const void *v, void *o, int B, int H, int N, int d,
+                               int dtype, const fvattn_csr *csr, const fvattn_attn_opts *opts, void *stream);
 
 #ifdef __cplusplus
 }

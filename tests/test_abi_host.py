@@ -13,7 +13,7 @@ import top_block_sparse_pooled_amd as fv
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fvattn.h")
 
-OK, INVALID, UNSUPPORTED, CAPACITY, WORKSPACE, OVERFLOW, HIP, MISMATCH = 0, -1, -2, -3, -4, -5, -6, -7
+OK, INVALID, UNSUPPORTED, CAPACITY, WORKSPACE, OVERFLOW, HIP, MISMATCH, SCRATCH = 0, -1, -2, -3, -4, -5, -6, -7, -8
 FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call here fails validation first
 
 # Fake device pointers must never reach a real launch: run these only where no GPU is visible.
@@ -49,7 +49,7 @@ def test_exports_every_declared_symbol(L):
 
 def test_version_and_strerror(L):
     assert L.fvattn_version() == 10100
-    for code in (OK, INVALID, UNSUPPORTED, CAPACITY, WORKSPACE, OVERFLOW, HIP, MISMATCH):
+    for code in (OK, INVALID, UNSUPPORTED, CAPACITY, WORKSPACE, OVERFLOW, HIP, MISMATCH, SCRATCH):
         s = L.fvattn_strerror(code).decode()
         assert s and s != "unknown error code"
     assert L.fvattn_strerror(42).decode() == "unknown error code"
@@ -246,3 +246,21 @@ def test_route_sasa_validation_order(L):
     assert need > L.fvattn_route_ws_bytes(1, 2, 1024, 64, 64, 64) + 2 * 16 * 16 * 8
     assert L.fvattn_route_sasa_ws_bytes(1, 2, 1024, 64, 64, 64, 3) == 0
     assert _route_sasa(L, _sopts(), ws_bytes=need - 1) == WORKSPACE
+
+
+def test_noalloc_validation(L):
+    """The no-allocation entry point validates like fvattn_sparse_attn and refuses problems larger
+    than its static scratch, all before touching the device."""
+    def call(B=1, H=2, N=1024, d=64, dt=0, csr=None, opts=None, v=FAKE):
+        c = csr if csr is not None else _csr(B * H, N)
+        return L.fvattn_sparse_attn_noalloc(FAKE, FAKE, v, FAKE, B, H, N, d, dt, ctypes.byref(c),
+                                            ctypes.byref(opts) if opts is not None else None, None)
+    assert call(dt=3) == UNSUPPORTED
+    assert call(v=None) == INVALID
+    assert call(N=1000, csr=_csr(2, 1024)) == MISMATCH
+    assert call(opts=fv._OptsC(9, 0, None, 0, -1, 0)) == INVALID
+    assert call(opts=fv._OptsC(0, 0, FAKE, 4 * 16 - 1, -1, 0)) == INVALID      # trace too small
+    assert L.fvattn_sparse_attn_noalloc(FAKE, FAKE, FAKE, FAKE, 1, 2, 1024, 64, 0, None, None, None) == INVALID
+    # 300 heads x 1280 query blocks = 384,000 rows > FVATTN_NOALLOC_MAX_ROWS (262,144)
+    assert call(H=300, N=81920, csr=_csr(300, 81920)) == SCRATCH
+    assert call(H=300, N=81920, csr=_csr(300, 81920), dt=7) == UNSUPPORTED   # argument checks come first

@@ -16,12 +16,14 @@ from typing import Optional
 __all__ = [
     "FvAttnError", "Csr", "lib", "version", "csr_max_nnz", "route_ws_bytes", "attn_ws_bytes",
     "pool", "route", "worklist", "sparse_attn", "attn_plan", "attn_run", "SCHED", "ws_status", "plan_worklist",
+    "sparse_attn_noalloc", "NOALLOC_MAX_ROWS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfvattn.so")
 
 BF16, F32 = 0, 1
+NOALLOC_MAX_ROWS = 262144   # FVATTN_NOALLOC_MAX_ROWS
 SCHED = {"lpt": 0, "identity": 1, "head_lpt": 2, "xcd": 3, "rlb": 4, "head_desc": 5}
 STATUS = {"select_nocross": 1, "plan_mismatch": 2}
 ROUTE_MODES = {"topp": 0, "topk": 1}
@@ -100,6 +102,9 @@ def lib() -> ctypes.CDLL:
         L.fvattn_attn_run.restype = i32
         L.fvattn_attn_run.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, ctypes.POINTER(_CsrC),
                                       ctypes.POINTER(_OptsC), vp, sz, vp]
+        L.fvattn_sparse_attn_noalloc.restype = i32
+        L.fvattn_sparse_attn_noalloc.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, ctypes.POINTER(_CsrC),
+                                                 ctypes.POINTER(_OptsC), vp]
         L.fvattn_sparse_attn.restype = i32
         L.fvattn_sparse_attn.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, ctypes.POINTER(_CsrC),
                                          ctypes.POINTER(_OptsC), vp, sz, vp]
@@ -344,6 +349,22 @@ def sparse_attn(q, k, v, csr: Csr, schedule: str = "identity", grid: int = 0, tr
     _check(lib().fvattn_sparse_attn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, N, d,
                                     _dtype_code(q), ctypes.byref(c), ctypes.byref(opts), ws.data_ptr(),
                                     ws.numel(), _stream(q.device)), "fvattn_sparse_attn")
+    return out
+
+
+def sparse_attn_noalloc(q, k, v, csr: Csr, schedule: str = "identity", grid: int = 0, trace=None, out=None,
+                        out_dtype=None):
+    """fvattn_sparse_attn_noalloc: as sparse_attn, with the plan in the library's static device
+    scratch instead of a workspace (B*H*nqb <= NOALLOC_MAX_ROWS; calls on one GPU must not overlap)."""
+    _check_qkv(q, k, v)
+    B, H, N, d = q.shape
+    out, odc = _attn_out(q, out, out_dtype)
+    tp, tcap = _trace_arg(trace)
+    opts = _OptsC(SCHED[schedule], grid, tp, tcap, odc, 0)
+    c = csr.c()
+    _check(lib().fvattn_sparse_attn_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, N, d,
+                                            _dtype_code(q), ctypes.byref(c), ctypes.byref(opts), _stream(q.device)),
+           "fvattn_sparse_attn_noalloc")
     return out
 
 

@@ -3,6 +3,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "common.h"
 
 namespace fv {
@@ -154,6 +156,7 @@ const char *fvattn_strerror(int code) {
     case FVATTN_ERR_OVERFLOW: return "problem size overflows 32-bit indexing";
     case FVATTN_ERR_HIP: return "HIP launch failure";
     case FVATTN_ERR_MISMATCH: return "CSR shape does not match the attention arguments";
+    case FVATTN_ERR_SCRATCH: return "more query-block rows than the no-allocation scratch holds (FVATTN_NOALLOC_MAX_ROWS)";
     default: return "unknown error code";
   }
 }
@@ -329,16 +332,24 @@ int fvattn_ws_status(const void *ws, int which, uint32_t *status, void *stream) 
 }
 
 namespace {
-// Validation shared by plan / run / sparse_attn.  Returns the workspace layout through *w.
-int attn_checks(const void *v, int B, int H, int N, int d, int dtype, const fvattn_csr *csr, Shape *s, void *ws,
-                size_t ws_bytes, AttnWs *w) {
+// Argument checks shared by plan / run / sparse_attn (everything but the workspace).
+int attn_arg_checks(const void *v, int B, int H, int N, int d, int dtype, const fvattn_csr *csr, Shape *s) {
   if (!dtype_ok(dtype)) return FVATTN_ERR_UNSUPPORTED;
   if (csr == nullptr) return FVATTN_ERR_INVALID;
   int rc = check_shape(B, H, N, d, csr->block_q, csr->block_k, s);
   if (rc != FVATTN_OK) return rc;
-  if (v == nullptr || ws == nullptr) return FVATTN_ERR_INVALID;
+  if (v == nullptr) return FVATTN_ERR_INVALID;
   if (csr->row_ptr == nullptr || csr->col_idx == nullptr) return FVATTN_ERR_INVALID;
   if (csr->bh != s->BH || csr->n != N || csr->nqb != s->nqb || csr->nkb != s->nkb) return FVATTN_ERR_MISMATCH;
+  return FVATTN_OK;
+}
+
+// The argument checks and the caller's workspace.  Returns the workspace layout through *w.
+int attn_checks(const void *v, int B, int H, int N, int d, int dtype, const fvattn_csr *csr, Shape *s, void *ws,
+                size_t ws_bytes, AttnWs *w) {
+  int rc = attn_arg_checks(v, B, H, N, d, dtype, csr, s);
+  if (rc != FVATTN_OK) return rc;
+  if (ws == nullptr) return FVATTN_ERR_INVALID;
   *w = attn_ws_layout(s->rows, (char *)ws);
   if (ws_bytes < w->bytes) return FVATTN_ERR_WORKSPACE;
   return FVATTN_OK;
@@ -439,3 +450,57 @@ int fvattn_sparse_attn(const void *q, const void *k, const void *v, void *o, int
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------------------
+// No-allocation variant of fvattn_sparse_attn: the attention workspace (plan control block,
+// work list, sort scratch) is the static device array `scratch`, sized for
+// FVATTN_NOALLOC_MAX_ROWS rows.  Host code never uses the array's name as a device address: on
+// a device's first call the address is taken with hipGetSymbolAddress (with that device
+// current) and kept per device.  The plan kernel writes every control word and work-list entry
+// it later reads, so nothing needs clearing between calls.
+// ---------------------------------------------------------------------------------------
+namespace {
+constexpr size_t kScratchBytes = 256 + 2 * (((size_t)FVATTN_NOALLOC_MAX_ROWS * sizeof(int32_t) + 255) & ~(size_t)255);
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_addr[kMaxDevices];
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+// Device address of this device's `scratch` (taken once per device).
+int scratch_address(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return FVATTN_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return FVATTN_ERR_UNSUPPORTED;
+  void *p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return FVATTN_ERR_HIP;
+    g_scratch_addr[dev].store(p, std::memory_order_release);   // racing first calls store the same address
+  }
+  *out = p;
+  return FVATTN_OK;
+}
+}  // namespace
+
+extern "C" int fvattn_sparse_attn_noalloc(const void *q, const void *k, const void *v, void *o, int B, int H, int N,
+                                          int d, int dtype, const fvattn_csr *csr, const fvattn_attn_opts *opts,
+                                          void *stream) {
+  // every argument check of fvattn_sparse_attn before the scratch address is taken
+  Shape s;
+  int rc = attn_arg_checks(v, B, H, N, d, dtype, csr, &s);
+  if (rc != FVATTN_OK) return rc;
+  if (s.rows > FVATTN_NOALLOC_MAX_ROWS || attn_ws_layout(s.rows, nullptr).bytes > kScratchBytes)
+    return FVATTN_ERR_SCRATCH;
+  const int sched = opts ? opts->schedule : FVATTN_SCHED_IDENTITY;
+  if ((rc = sched_ok(sched, s)) != FVATTN_OK) return rc;
+  int grid, out_dt;
+  uint64_t *trace;
+  if ((rc = run_checks(q, k, o, dtype, s, opts, &grid, &trace, &out_dt)) != FVATTN_OK) return rc;
+  void *ws = nullptr;
+  if ((rc = scratch_address(&ws)) != FVATTN_OK) return rc;
+  const AttnWs w = attn_ws_layout(s.rows, (char *)ws);
+  hipStream_t st = (hipStream_t)stream;
+  if ((rc = do_plan(s, dtype, csr, sched, w, st)) != FVATTN_OK) return rc;
+  return do_run(q, k, v, o, s, dtype, out_dt, csr, grid, trace, w, st);
+}
