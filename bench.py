@@ -113,7 +113,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="wan14b_n32760")
     ap.add_argument("--p", type=float, default=None)
-    ap.add_argument("--schedule", default="identity", choices=sorted(SCHEDULES))
+    ap.add_argument("--schedule", default="head_desc", choices=sorted(SCHEDULES),
+                    help="attention work order (the library default is head_desc: heads heaviest first)")
     ap.add_argument("--alt-p", type=float, default=0.95,
                     help="also time the layer at this p (the workload's second threshold); 0: off")
     ap.add_argument("--out", default="bf16", choices=["f32", "bf16"],

@@ -59,6 +59,7 @@ enum {
  * its rows keep.  Head loads are the per-head loads of the FVAttn summary's RLB section.
  */
 enum {
+  FVATTN_SCHED_DEFAULT = -1, /* HEAD_DESC for up to 4096 heads, else IDENTITY                 */
   FVATTN_SCHED_LPT = 0,      /* units by work, longest first, ties by unit id                 */
   FVATTN_SCHED_IDENTITY = 1, /* units in ascending id (head-major) order                      */
   FVATTN_SCHED_HEAD_LPT = 2, /* heads by load (heaviest first, ties by id), a head's units
@@ -108,11 +109,13 @@ typedef struct fvattn_csr {
 } fvattn_csr;
 
 /*
- * Options of fvattn_sparse_attn; pass NULL for the defaults (identity order, library grid,
- * no trace).  The identity order is the fastest measured on MI355X: with one workgroup per
- * CU, the units in flight are those of one head, whose K/V tiles then share the caches.
- * LPT balances the per-CU load best but mixes heads.
- *   schedule  one of FVATTN_SCHED_*.
+ * Options of fvattn_sparse_attn; pass NULL for the defaults (FVATTN_SCHED_DEFAULT, library
+ * grid, no trace).  The default order takes the heads heaviest first (the FVAttn summary's RLB
+ * moves the heaviest heads first) and a head's units in id order: with one workgroup per CU the
+ * units in flight then belong to one head, whose K/V tiles share the caches.  Measured on MI355X
+ * it runs as fast as the identity order and faster than LPT, which balances CUs best but mixes
+ * heads.
+ *   schedule  one of FVATTN_SCHED_* (negative: FVATTN_SCHED_DEFAULT).
  *   grid      number of persistent workgroups; 0 = as many as stay resident.
  *   trace     optional device array of uint64.  Record t (t < units) describes the t-th work
  *             unit taken: {hardware id (XCC_ID << 32 | HW_ID), start clock, end clock, unit id},

@@ -92,6 +92,17 @@ SMALL = [
                                                                 "bf16", (21, 30, 35)), 0.85),
     ("bf16_h1_n75600_nkb1182", lambda: workloads.small_case(1, 75600, 128, 64, 64, 27, ("uniform", 0.0, 3.0),
                                                             "bf16", (21, 45, 80)), 0.9),
+    # more heads (B*H = 8, 16, 24)
+    ("bf16_h8_n3000", lambda: workloads.small_case(8, 3000, 128, 64, 64, 35, ("uniform", 0.0, 4.0),
+                                                         "bf16", (3, 20, 50)), 0.9),
+    ("bf16_h16_n1500_d64_bk32", lambda: workloads.small_case(16, 1500, 64, 64, 32, 36, ("uniform", 0.5, 3.0),
+                                                                   "bf16", (3, 10, 50)), 0.85),
+    ("f32_h8_n700_bq128", lambda: workloads.small_case(8, 700, 128, 128, 64, 37, ("uniform", 0.0, 3.0),
+                                                             "f32", (7, 10, 10)), 0.9),
+    ("bf16_h8_n22050_bk32_nkb690", lambda: workloads.small_case(8, 22050, 128, 64, 32, 38, ("uniform", 0.0, 3.0),
+                                                                      "bf16", (21, 30, 35)), 0.85),
+    ("bf16_h24_n4000_bq128", lambda: workloads.small_case(24, 4000, 128, 128, 64, 39, ("loguniform", 0.1, 6.0),
+                                                                "bf16", (4, 20, 50)), 0.95),
 ]
 
 

@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(_HERE, "libfvattn.so")
 
 BF16, F32 = 0, 1
 NOALLOC_MAX_ROWS = 262144   # FVATTN_NOALLOC_MAX_ROWS
-SCHED = {"lpt": 0, "identity": 1, "head_lpt": 2, "xcd": 3, "rlb": 4, "head_desc": 5}
+SCHED = {"default": -1, "lpt": 0, "identity": 1, "head_lpt": 2, "xcd": 3, "rlb": 4, "head_desc": 5}
 STATUS = {"select_nocross": 1, "plan_mismatch": 2}
 ROUTE_MODES = {"topp": 0, "topk": 1}
 
@@ -328,7 +328,7 @@ def _trace_arg(trace):
     return trace.data_ptr(), trace.numel()
 
 
-def sparse_attn(q, k, v, csr: Csr, schedule: str = "identity", grid: int = 0, trace=None, out=None, ws=None,
+def sparse_attn(q, k, v, csr: Csr, schedule: str = "default", grid: int = 0, trace=None, out=None, ws=None,
                 out_dtype=None):
     """Block-sparse attention over the CSR's kept blocks -> o [B, H, N, d].
     out_dtype: None (dtype of q) or torch.float32 (accumulator precision, for bf16 inputs)."""
@@ -352,7 +352,7 @@ def sparse_attn(q, k, v, csr: Csr, schedule: str = "identity", grid: int = 0, tr
     return out
 
 
-def sparse_attn_noalloc(q, k, v, csr: Csr, schedule: str = "identity", grid: int = 0, trace=None, out=None,
+def sparse_attn_noalloc(q, k, v, csr: Csr, schedule: str = "default", grid: int = 0, trace=None, out=None,
                         out_dtype=None):
     """fvattn_sparse_attn_noalloc: as sparse_attn, with the plan in the library's static device
     scratch instead of a workspace (B*H*nqb <= NOALLOC_MAX_ROWS; calls on one GPU must not overlap)."""
@@ -385,7 +385,7 @@ def attn_ws(q, csr: Csr):
     return torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
 
 
-def attn_plan(v, csr: Csr, ws, schedule: str = "identity"):
+def attn_plan(v, csr: Csr, ws, schedule: str = "default"):
     """Work list of the CSR rows into ws (v supplies the shape only); see fvattn_attn_plan."""
     _check_qkv(v)
     B, H, N, d = v.shape

@@ -5,7 +5,7 @@
 
 #include <atomic>
 
-#include "common.h"
+#include "routing.h"
 
 namespace fv {
 int launch_pool(const void *x, int BH, int N, int d, int dtype, int block, double *out, hipStream_t st);
@@ -16,10 +16,7 @@ size_t sasa_hist_bytes(int R);
 int launch_sasa(const double *imp, uint32_t *bitmask, int32_t *counts, int32_t *bsum, int32_t *head_load, int nkw,
                 int nqb, int nkb, int BH, int R, int critical, double alpha, double tau, void *grp_buf,
                 uint32_t *ghist, int32_t *tiecnt, int32_t *tiepre, int32_t *added_out, hipStream_t st);
-int launch_select(const void *q, const double *ksw, int BH, int d, int dtype, int nqb, int nkb, double p,
-                  int32_t *counts, uint32_t *bitmask, int nkw, int32_t *head_load, int32_t *bsum, int mode, int topk,
-                  int k_min, int k_max, int window, int bq, int bk, int N, double *imp, uint32_t *status,
-                  hipStream_t st);
+
 int launch_csr(const int32_t *counts, const uint32_t *bitmask, const int32_t *bsum, int rows, int nkw, int nkb,
                int32_t *row_ptr, int32_t *col_idx, hipStream_t st);
 int launch_plan(const int32_t *row_ptr, int rows, int nqb, int nkb, int G, int sched, int32_t *wl, int32_t *tmp,
@@ -213,15 +210,28 @@ int route_core(const void *q, const void *k, const Shape &s, int N, int d, int d
                hipStream_t st) {
   int rc;
   csr->bh = s.BH; csr->n = N; csr->block_q = block_q; csr->block_k = block_k; csr->nqb = s.nqb; csr->nkb = s.nkb;
-  if ((rc = fv::launch_pool_k(k, s.BH, N, d, dtype, block_k, w.ksw, w.bsum, w.nblk, csr->head_load, s.BH,
-                              (int32_t *)w.status, 1, st)) != FVATTN_OK)
-    return rc;
-  const double p = o.mode == FVATTN_ROUTE_TOPP ? o.p : 1.0;
-  if ((rc = fv::launch_select(q, w.ksw, s.BH, d, dtype, s.nqb, s.nkb, p, w.counts, w.bitmask, s.nkw, csr->head_load,
-                              w.bsum, o.mode, o.topk, o.k_min, o.k_max, o.window, block_q, block_k, N, imp, w.status,
-                              st)) !=
-      FVATTN_OK)
-    return rc;
+  fv::RouteLaunch r;
+  r.q = q;
+  r.k = k;
+  r.ksw = w.ksw;
+  r.BH = s.BH;
+  r.N = N;
+  r.d = d;
+  r.dtype = dtype;
+  r.bq = block_q;
+  r.bk = block_k;
+  r.nqb = s.nqb;
+  r.nkb = s.nkb;
+  r.nkw = s.nkw;
+  r.p = o.mode == FVATTN_ROUTE_TOPP ? o.p : 1.0;
+  r.counts = w.counts;
+  r.bitmask = w.bitmask;
+  r.head_load = csr->head_load;
+  r.bsum = w.bsum;
+  r.nbsum = w.nblk;
+  r.sel = fv::SelOpts{o.mode, o.topk, o.k_min, o.k_max, o.window, block_q, block_k, N, imp};
+  r.status = w.status;
+  if ((rc = fv::launch_route(r, st)) != FVATTN_OK) return rc;
   if (!csr_after) return FVATTN_OK;
   return fv::launch_csr(w.counts, w.bitmask, w.bsum, s.rows, s.nkw, s.nkb, csr->row_ptr, csr->col_idx, st);
 }
@@ -355,6 +365,13 @@ int attn_checks(const void *v, int B, int H, int N, int d, int dtype, const fvat
   return FVATTN_OK;
 }
 
+// FVATTN_SCHED_DEFAULT (any negative value): heads heaviest first (HEAD_DESC) while the plan can
+// rank the heads on the device, else identity.
+int resolve_sched(int sched, const Shape &s) {
+  if (sched >= 0) return sched;
+  return s.BH <= kMaxPlanHeads ? FVATTN_SCHED_HEAD_DESC : FVATTN_SCHED_IDENTITY;
+}
+
 int sched_ok(int sched, const Shape &s) {
   if (!sched_known(sched)) return FVATTN_ERR_INVALID;
   if (sched_by_head(sched) && s.BH > kMaxPlanHeads) return FVATTN_ERR_UNSUPPORTED;
@@ -416,6 +433,7 @@ int fvattn_attn_plan(const void *v, int B, int H, int N, int d, int dtype, const
   AttnWs w;
   int rc = attn_checks(v, B, H, N, d, dtype, csr, &s, ws, ws_bytes, &w);
   if (rc != FVATTN_OK) return rc;
+  schedule = resolve_sched(schedule, s);
   if ((rc = sched_ok(schedule, s)) != FVATTN_OK) return rc;
   return do_plan(s, dtype, csr, schedule, w, (hipStream_t)stream);
 }
@@ -439,7 +457,7 @@ int fvattn_sparse_attn(const void *q, const void *k, const void *v, void *o, int
   AttnWs w;
   int rc = attn_checks(v, B, H, N, d, dtype, csr, &s, ws, ws_bytes, &w);
   if (rc != FVATTN_OK) return rc;
-  const int sched = opts ? opts->schedule : FVATTN_SCHED_IDENTITY;
+  const int sched = resolve_sched(opts ? opts->schedule : FVATTN_SCHED_DEFAULT, s);
   if ((rc = sched_ok(sched, s)) != FVATTN_OK) return rc;
   int grid, out_dt;
   uint64_t *trace;
@@ -492,7 +510,7 @@ extern "C" int fvattn_sparse_attn_noalloc(const void *q, const void *k, const vo
   if (rc != FVATTN_OK) return rc;
   if (s.rows > FVATTN_NOALLOC_MAX_ROWS || attn_ws_layout(s.rows, nullptr).bytes > kScratchBytes)
     return FVATTN_ERR_SCRATCH;
-  const int sched = opts ? opts->schedule : FVATTN_SCHED_IDENTITY;
+  const int sched = resolve_sched(opts ? opts->schedule : FVATTN_SCHED_DEFAULT, s);
   if ((rc = sched_ok(sched, s)) != FVATTN_OK) return rc;
   int grid, out_dt;
   uint64_t *trace;

@@ -108,12 +108,6 @@ __device__ __forceinline__ uint64_t hw_id_word() {
 // compiler from moving memory accesses across it.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// s_waitcnt on the vector memory counter only (expcnt and lgkmcnt fields at their maxima).
-template <int NV>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(NV >= 0 && NV < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((NV & 15) | ((NV >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 
 template <int BQ, int BK, int D>
 __global__ __launch_bounds__(512, 1) void k_attn_pp(

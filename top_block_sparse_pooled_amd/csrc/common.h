@@ -71,6 +71,13 @@ __device__ __forceinline__ int digit_shift(unsigned long long width) {
   return wm1 < 256ull ? 0 : 64 - __clzll((long long)wm1) - 8;
 }
 
+// s_waitcnt on the vector memory counter only (expcnt and lgkmcnt fields at their maxima).
+template <int NV>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(NV >= 0 && NV < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((NV & 15) | ((NV >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // Compute units of the current device (cached per device); 0 on success.
 inline int device_cus(int *cus) {
   // per-device cache; concurrent callers may both query and store the same value

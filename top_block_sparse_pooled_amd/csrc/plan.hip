@@ -193,9 +193,25 @@ __global__ __launch_bounds__(1024) void k_plan(PlanArgs a) {
     return;
   }
   // head-ordered schedules: rank heads by load descending, ties by head id (nh <= kPlMaxHeads)
-  const unsigned maxl = (unsigned)a.nqb * (unsigned)a.nkb;
-  lsd_sort(nh, bits_for(maxl), [&](int h) { return (int)(maxl - (unsigned)um.head_load(h)); }, s.ha, s.hb, s);
-  for (int r = tid; r < nh; r += 1024) s.hkey[s.ha[r]] = r;   // rank of each head
+  if (nh <= 1024) {
+    // one pass: thread h counts the heads that go before it
+    for (int h = tid; h < nh; h += 1024) s.hb[h] = um.head_load(h);
+    __syncthreads();
+    if (tid < nh) {
+      const int lh = s.hb[tid];
+      int rank = 0;
+      for (int h2 = 0; h2 < nh; ++h2) {
+        const int l2 = s.hb[h2];
+        rank += (l2 > lh) || (l2 == lh && h2 < tid);
+      }
+      s.hkey[tid] = rank;
+      s.ha[rank] = tid;
+    }
+  } else {
+    const unsigned maxl = (unsigned)a.nqb * (unsigned)a.nkb;
+    lsd_sort(nh, bits_for(maxl), [&](int h) { return (int)(maxl - (unsigned)um.head_load(h)); }, s.ha, s.hb, s);
+    for (int r = tid; r < nh; r += 1024) s.hkey[s.ha[r]] = r;   // rank of each head
+  }
   __syncthreads();
   if (a.sched == FVATTN_SCHED_HEAD_LPT) {
     const int hb = bits_for((unsigned)(nh - 1));

@@ -29,7 +29,7 @@
 //  * k_csr       exclusive scan of per-row counts (a row's offset is the per-64-row sums
 //                before its block plus a lane scan inside it, no second pass) and expansion
 //                of the kept-bit masks into ascending column indices.
-#include "common.h"
+#include "routing.h"
 
 namespace fv {
 
@@ -167,14 +167,8 @@ __global__ __launch_bounds__(256) void k_pool(PoolArgs a) {
 // ---------------------------------------------------------------------------------------
 constexpr int kMaxNkw = 40;  // 1280 key blocks
 
-// Routing variant of k_select (see fvattn_route_opts): mode, top-k count, clamp of the Top-p
-// count, local window, and the block geometry the window needs.
-struct SelOpts {
-  int mode, topk, k_min, k_max, window, bq, bk, N;
-  double *imp;   // optional [rows][nkb]: importance P of every block (SASA candidates); EXT only
-};
-
 constexpr double kFix52 = 4503599627370496.0;  // 2^52: masses as fixed point
+
 
 // Kept set of one row by the wave: the shortest prefix of the (e descending, index ascending)
 // order whose mass (bycnt = false: fixed-point e, target T) or count (bycnt = true, target T)
@@ -292,64 +286,81 @@ __device__ __forceinline__ uint32_t select_row(const double (&ev)[NPL], int nkb,
   return word;
 }
 
+// Arguments of one select item.
+struct SelArgs {
+  const void *qraw;
+  const double *ksw;
+  int nqb, nkb, nkw;
+  double scale, p;
+  int32_t *counts;
+  uint32_t *bitmask;
+  int32_t *head_load, *bsum;
+  SelOpts sel;
+  uint32_t *status;
+};
+
+// LDS of a select workgroup: NWV waves, MAXT key tiles of 16 per wave.
+template <typename T, int D, int MAXT, int NWV>
+struct SelLds {
+  static constexpr int KCAP = 16 * NWV * MAXT;   // key blocks the tiles cover
+  static constexpr int RB = NWV == 4 ? 16 : 8;   // rows staged at once
+  // staged rows; before them, the item's pooled query blocks (16 D doubles)
+  static constexpr int ESZ = RB * KCAP > 16 * D ? RB * KCAP : 16 * D;
+  double eq[ESZ];
+  unsigned long long h_mass[NWV][256];
+  uint32_t h_cnt[NWV][256];
+  double part[NWV][16];
+  unsigned long long zpart[NWV][16];
+  double minpart[NWV][16];
+  int cnt[16];   // kept counts of the item's rows
+};
+
+// One select item: scores, softmax and the Top-p cut (or a routing variant) for query blocks
+// 16 g .. 16 g + 15 of head bh, by the whole workgroup.
+//   1. The item's query blocks are mean-pooled straight into LDS (same summation order as
+//      k_pool); the raw Q reads of one workgroup overlap the compute phases of the others.
+//   2. Scores for the 16 rows on the float64 MFMA, wave w holding key tiles w, w + NWV, ...;
+//      row maxima, e = exp(s - max), fixed-point row sums Z and row minima of e across the
+//      waves (two workgroup barriers).
+//   3. The e values go to LDS as whole rows (RB rows at a time), and each wave then resolves
+//      its rows alone: the row's values sit in registers (lane l: key blocks l + 64 t), the
+//      radix passes use a histogram private to the wave, and the kept set leaves as 64-bit
+//      ballots.  No workgroup barrier inside the selection.
+// Outputs counts[row] and the kept-bit mask bitmask[row][nkw]; adds loads to head_load and bsum.
 template <typename T, int D, int MAXT, int NWV, bool EXT>
-__global__ __launch_bounds__(64 * NWV, NWV == 4 ? 2 : 1) void k_select(const void *__restrict__ qraw,
-                                                const double *__restrict__ ksw, int nqb, int nkb,
-                                                double scale, double p, int32_t *__restrict__ counts,
-                                                uint32_t *__restrict__ bitmask, int nkw,
-                                                int32_t *__restrict__ head_load, int32_t *__restrict__ bsum,
-                                                int BH, SelOpts sel, uint32_t *__restrict__ status) {
+__device__ __forceinline__ void select_item(SelLds<T, D, MAXT, NWV> &L, const SelArgs &a, int bh, int g) {
   constexpr int KS = D / 4;               // MFMA k-steps
-  constexpr int KCAP = 16 * NWV * MAXT;   // key blocks the tiles cover
+  constexpr int KCAP = SelLds<T, D, MAXT, NWV>::KCAP;
   constexpr int NPL = KCAP / 64;          // values per lane in the row phase
-  constexpr int RB = NWV == 4 ? 16 : 8;   // rows staged in LDS at once
+  constexpr int RB = SelLds<T, D, MAXT, NWV>::RB;
   constexpr int NB = 16 / RB;
   constexpr int RPW = RB / NWV;           // rows per wave per batch
   static_assert(KCAP % 64 == 0 && RB % NWV == 0 && (RB / 4) * 4 == RB, "row phase geometry");
   constexpr int EPC = DT<T>::per16, CPR = D / EPC;
-  // staged rows; before them, the item's pooled query blocks (16 D doubles)
-  constexpr int ESZ = RB * KCAP > 16 * D ? RB * KCAP : 16 * D;
-  __shared__ double s_eq[ESZ];
-  double(*s_e)[KCAP] = reinterpret_cast<double(*)[KCAP]>(s_eq);
-  __shared__ unsigned long long h_mass[NWV][256];
-  __shared__ uint32_t h_cnt[NWV][256];
-  __shared__ double s_part[NWV][16];
-  __shared__ unsigned long long s_zpart[NWV][16];
-  __shared__ double s_minpart[NWV][16];
-  __shared__ int s_cnt[16];           // kept counts of the item's rows
-
+  double(*s_e)[KCAP] = reinterpret_cast<double(*)[KCAP]>(L.eq);
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int nqg = (nqb + 15) >> 4;
+  const int nqb = a.nqb, nkb = a.nkb, nkw = a.nkw;
   const int nkt = (nkb + 15) >> 4;
-
-  // Persistent loop over items (head bh, group g of 16 query blocks).  Workgroup b runs on
-  // XCD b % 8 (round-robin dispatch); XCD x owns the x-th eighth of the items in head-major
-  // order, so its L2 holds the pooled keys of only a few heads.  gridDim.x >= 8.
-  const int items = BH * nqg;
-  const int xcd = blockIdx.x & 7;
-  const int nwx = ((int)gridDim.x - xcd + 7) >> 3;
-  const int it_end = (int)((long long)items * (xcd + 1) / 8);
-  for (int it = (int)((long long)items * xcd / 8) + (int)(blockIdx.x >> 3); it < it_end; it += nwx) {
-  const int bh = it / nqg, g = it - bh * nqg;
+  (void)tid;
 
   // ---- the item's 16 query blocks, mean-pooled straight into LDS in the float64 MFMA
   // operand order (block jj, dim c at (c / 4) 64 + jj + 16 (c % 4)); the raw Q reads of one
   // workgroup overlap the score phases of the others
   {
-    const T *xh = reinterpret_cast<const T *>(qraw) + (size_t)bh * sel.N * D;
+    const T *xh = reinterpret_cast<const T *>(a.qraw) + (size_t)bh * a.sel.N * D;
     // two blocks per wave at a time: 32 loads in flight per lane
     constexpr int NBK = NWV == 4 ? 2 : 1;
     for (int jj = w; jj < 16; jj += NBK * NWV) {
       double m[NBK][EPC];
-      pool_blocks<T, D, NBK>(xh, 16 * g + jj, NWV, sel.bq, nqb, sel.N, m);
+      pool_blocks<T, D, NBK>(xh, 16 * g + jj, NWV, a.sel.bq, nqb, a.sel.N, m);
       if (lane < CPR) {
 #pragma unroll
         for (int b = 0; b < NBK; ++b)
 #pragma unroll
           for (int e = 0; e < EPC; ++e) {
             const int cc = lane * EPC + e;
-            s_eq[(cc >> 2) * 64 + jj + b * NWV + 16 * (cc & 3)] = m[b][e];
+            L.eq[(cc >> 2) * 64 + jj + b * NWV + 16 * (cc & 3)] = m[b][e];
           }
       }
     }
@@ -361,7 +372,7 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 ? 2 : 1) void k_select(const voi
 #pragma unroll
   for (int k = 0; k < MAXT; ++k) acc[k] = d4{0.0, 0.0, 0.0, 0.0};
   {
-    const double *qa = s_eq + lane;
+    const double *qa = L.eq + lane;
     // k-step outer, tiles inner: MAXT independent accumulators.  The operands of PF k-steps
     // (one of qbar, MAXT of kbar each) are in flight ahead of the MFMAs that use them, which
     // covers the L2 latency of the pooled keys.  Tiles past the last read a valid tile (their
@@ -369,7 +380,7 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 ? 2 : 1) void k_select(const voi
     constexpr int PF = MAXT >= 8 ? 1 : 3;
     const double *kb[MAXT];
 #pragma unroll
-    for (int k = 0; k < MAXT; ++k) kb[k] = ksw + ((size_t)(bh * nkt + min(w + NWV * k, nkt - 1)) * KS) * 64 + lane;
+    for (int k = 0; k < MAXT; ++k) kb[k] = a.ksw + ((size_t)(bh * nkt + min(w + NWV * k, nkt - 1)) * KS) * 64 + lane;
     double abuf[PF], bbuf[PF][MAXT];
 #pragma unroll
     for (int s = 0; s < PF; ++s) {
@@ -404,7 +415,7 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 ? 2 : 1) void k_select(const voi
     const int j = 16 * (w + NWV * k) + jl;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      acc[k][v] *= scale;
+      acc[k][v] *= a.scale;
       if (j < nkb) mx[v] = fmax(mx[v], acc[k][v]);
     }
   }
@@ -412,15 +423,15 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 ? 2 : 1) void k_select(const voi
   for (int v = 0; v < 4; ++v) {
 #pragma unroll
     for (int off = 8; off >= 1; off >>= 1) mx[v] = fmax(mx[v], __shfl_xor(mx[v], off, 16));
-    if (jl == 0) s_part[w][ig + 4 * v] = mx[v];
+    if (jl == 0) L.part[w][ig + 4 * v] = mx[v];
   }
   __syncthreads();
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     const int r = ig + 4 * v;
-    double m = s_part[0][r];
+    double m = L.part[0][r];
 #pragma unroll
-    for (int ww = 1; ww < NWV; ++ww) m = fmax(m, s_part[ww][r]);
+    for (int ww = 1; ww < NWV; ++ww) m = fmax(m, L.part[ww][r]);
     mx[v] = m;
   }
 
@@ -446,8 +457,8 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 ? 2 : 1) void k_select(const voi
       mn[v] = fmin(mn[v], __shfl_xor(mn[v], off, 16));
     }
     if (jl == 0) {
-      s_zpart[w][ig + 4 * v] = zs[v];
-      s_minpart[w][ig + 4 * v] = mn[v];
+      L.zpart[w][ig + 4 * v] = zs[v];
+      L.minpart[w][ig + 4 * v] = mn[v];
     }
   }
 
@@ -466,7 +477,7 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 ? 2 : 1) void k_select(const voi
       const int r = b * RB + rr * NWV + w;
       const int i = 16 * g + r;
       if (i >= nqb) {   // wave-uniform
-        if (lane == 0) s_cnt[r] = 0;
+        if (lane == 0) L.cnt[r] = 0;
         continue;
       }
       const size_t row = (size_t)bh * nqb + i;
@@ -477,62 +488,62 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 ? 2 : 1) void k_select(const voi
       double emin = 1.0;
 #pragma unroll
       for (int ww = 0; ww < NWV; ++ww) {
-        Z += s_zpart[ww][r];
-        emin = fmin(emin, s_minpart[ww][r]);
+        Z += L.zpart[ww][r];
+        emin = fmin(emin, L.minpart[ww][r]);
       }
       const unsigned long long lo0 = (unsigned long long)__double_as_longlong(emin);
       // search by mass (Top-p) or by count (top-k, or a clamped Top-p count)
       bool bycnt = false;
       unsigned long long tgt0;
       bool all;
-      if (EXT && sel.mode == FVATTN_ROUTE_TOPK) {
+      if (EXT && a.sel.mode == FVATTN_ROUTE_TOPK) {
         bycnt = true;
-        tgt0 = (unsigned long long)sel.topk;
-        all = sel.topk >= nkb;
+        tgt0 = (unsigned long long)a.sel.topk;
+        all = a.sel.topk >= nkb;
       } else {
-        tgt0 = (unsigned long long)ceil(p * (double)Z);
+        tgt0 = (unsigned long long)ceil(a.p * (double)Z);
         if (tgt0 > Z) tgt0 = Z;
         if (tgt0 < 1) tgt0 = 1;
-        all = p >= 1.0;
+        all = a.p >= 1.0;
       }
       int c;
       // lane L < nkw holds kept word L (key blocks 32 L .. 32 L + 31)
-      uint32_t word = select_row<NPL>(ev, nkb, bycnt, tgt0, lo0, all, h_mass[w], h_cnt[w], status, c);
-      if (EXT && !bycnt && (sel.k_min > 1 || sel.k_max > 0)) {
+      uint32_t word = select_row<NPL>(ev, nkb, bycnt, tgt0, lo0, all, L.h_mass[w], L.h_cnt[w], a.status, c);
+      if (EXT && !bycnt && (a.sel.k_min > 1 || a.sel.k_max > 0)) {
         // clamp of the Top-p count: re-select by count when it lies outside [k_min, k_max]
-        int tgt = max(c, sel.k_min);
-        if (sel.k_max > 0) tgt = min(tgt, sel.k_max);
+        int tgt = max(c, a.sel.k_min);
+        if (a.sel.k_max > 0) tgt = min(tgt, a.sel.k_max);
         tgt = min(tgt, nkb);
         if (tgt != c)
-          word = select_row<NPL>(ev, nkb, true, (unsigned long long)tgt, lo0, tgt >= nkb, h_mass[w], h_cnt[w], status,
+          word = select_row<NPL>(ev, nkb, true, (unsigned long long)tgt, lo0, tgt >= nkb, L.h_mass[w], L.h_cnt[w], a.status,
                                  c);
       }
-      if (EXT && sel.window > 0 && lane < nkw) {
+      if (EXT && a.sel.window > 0 && lane < nkw) {
         // local window: key blocks within `window` of those overlapping the query block's tokens
-        const int t0 = i * sel.bq, t1 = min(t0 + sel.bq, sel.N) - 1;
-        const int ja = max(0, t0 / sel.bk - sel.window), jb = min(nkb - 1, t1 / sel.bk + sel.window);
+        const int t0 = i * a.sel.bq, t1 = min(t0 + a.sel.bq, a.sel.N) - 1;
+        const int ja = max(0, t0 / a.sel.bk - a.sel.window), jb = min(nkb - 1, t1 / a.sel.bk + a.sel.window);
         const int lo_j = max(ja, 32 * lane), hi_j = min(jb, 32 * lane + 31);
         if (lo_j <= hi_j) {
           const int nbits = hi_j - lo_j + 1;
           word |= (nbits == 32 ? 0xffffffffu : ((1u << nbits) - 1u)) << (lo_j - 32 * lane);
         }
       }
-      if (EXT && sel.window > 0) {
+      if (EXT && a.sel.window > 0) {
         c = __popc(word);
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) c += __shfl_xor(c, off);
       }
-      if (lane < nkw) bitmask[row * nkw + lane] = word;
+      if (lane < nkw) a.bitmask[row * nkw + lane] = word;
       if (lane == 0) {
-        counts[row] = c;
-        s_cnt[r] = c;
+        a.counts[row] = c;
+        L.cnt[r] = c;
       }
-      if (EXT && sel.imp != nullptr) {
+      if (EXT && a.sel.imp != nullptr) {
         // importance of every block: the candidates' order for SASA
         const double invz = Z > 0 ? kFix52 / (double)Z : 0.0;   // 1 / Z with Z in 2^-52 units
 #pragma unroll
         for (int t = 0; t < NPL; ++t)
-          if (lane + 64 * t < nkb) sel.imp[row * nkb + lane + 64 * t] = ev[t] * invz;
+          if (lane + 64 * t < nkb) a.sel.imp[row * nkb + lane + 64 * t] = ev[t] * invz;
       }
     }
     __syncthreads();   // staged rows and partial sums consumed before they are overwritten
@@ -541,7 +552,7 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 ? 2 : 1) void k_select(const voi
     // the item's load of the head and its per-64-row sums for the CSR scan (the 16 rows
     // span at most two 64-row blocks)
     const size_t row0 = (size_t)bh * nqb + 16 * g;
-    const int c = lane < 16 ? s_cnt[lane] : 0;
+    const int c = lane < 16 ? L.cnt[lane] : 0;
     const bool second = lane < 16 && ((row0 + lane) >> 6) != (row0 >> 6);
     int c0 = second ? 0 : c, c1 = second ? c : 0;
 #pragma unroll
@@ -550,11 +561,27 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 ? 2 : 1) void k_select(const voi
       c1 += __shfl_xor(c1, off);
     }
     if (lane == 0) {
-      atomicAdd(&head_load[bh], c0 + c1);
-      atomicAdd(&bsum[row0 >> 6], c0);
-      if (c1 != 0) atomicAdd(&bsum[(row0 >> 6) + 1], c1);
+      atomicAdd(&a.head_load[bh], c0 + c1);
+      atomicAdd(&a.bsum[row0 >> 6], c0);
+      if (c1 != 0) atomicAdd(&a.bsum[(row0 >> 6) + 1], c1);
     }
   }
+}
+
+// Persistent select over all items (head bh, group g of 16 query blocks).  Workgroup b runs on
+// XCD b % 8 (round-robin dispatch); XCD x owns the x-th eighth of the items in head-major
+// order, so its L2 holds the pooled keys of only a few heads.  gridDim.x >= 8.
+template <typename T, int D, int MAXT, int NWV, bool EXT>
+__global__ __launch_bounds__(64 * NWV, NWV == 4 ? 2 : 1) void k_select(SelArgs a, int BH) {
+  __shared__ SelLds<T, D, MAXT, NWV> L;
+  const int nqg = (a.nqb + 15) >> 4;
+  const int items = BH * nqg;
+  const int xcd = blockIdx.x & 7;
+  const int nwx = ((int)gridDim.x - xcd + 7) >> 3;
+  const int it_end = (int)((long long)items * (xcd + 1) / 8);
+  for (int it = (int)((long long)items * xcd / 8) + (int)(blockIdx.x >> 3); it < it_end; it += nwx) {
+    const int bh = it / nqg, g = it - bh * nqg;
+    select_item<T, D, MAXT, NWV, EXT>(L, a, bh, g);
   }
 }
 
@@ -663,60 +690,52 @@ int launch_pool_k(const void *k, int BH, int N, int d, int dtype, int block_k, d
   return launch_pool_args(pa, BH, d, dtype, st);
 }
 
-template <typename T, int D, int MT, int NWV>
-static int launch_select_mt(const void *q, const double *ksw, int BH, int nqb, int nkb, double p, int32_t *counts,
-                            uint32_t *bitmask, int nkw, int32_t *head_load, int32_t *bsum, const SelOpts &sel,
-                            uint32_t *status, hipStream_t st) {
-  auto kern = (sel.mode != FVATTN_ROUTE_TOPP || sel.k_min > 1 || sel.k_max > 0 || sel.window > 0 ||
-               sel.imp != nullptr)
-                  ? k_select<T, D, MT, NWV, true>
-                  : k_select<T, D, MT, NWV, false>;
+// Pooling of K (k_pool, which also zeroes the per-64-row sums, head loads and status word), then
+// the persistent select over all items.
+template <typename T, int D, int MT, int NWV, bool EXT>
+static int launch_route_k(const RouteLaunch &r, hipStream_t st) {
+  const SelArgs a{r.q, r.ksw, r.nqb, r.nkb, r.nkw, 1.0 / sqrt((double)D), r.p, r.counts, r.bitmask, r.head_load,
+                  r.bsum, r.sel, r.status};
+  int rc = launch_pool_k(r.k, r.BH, r.N, D, r.dtype, r.bk, r.ksw, r.bsum, r.nbsum, r.head_load, r.BH,
+                         (int32_t *)r.status, 1, st);
+  if (rc != FVATTN_OK) return rc;
+  auto kern = k_select<T, D, MT, NWV, EXT>;
   int cus = 0, occ = 0;
   if (device_cus(&cus) != 0) return FVATTN_ERR_HIP;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, 64 * NWV, 0) != hipSuccess) return FVATTN_ERR_HIP;
-  const int items = cdiv(nqb, 16) * BH;
+  const int items = cdiv(r.nqb, 16) * r.BH;
   int grid = cus * (occ > 0 ? occ : 1);
   if (grid > items) grid = items;
   if (grid < 8) grid = 8;   // every XCD range needs a worker
-  const double scale = 1.0 / sqrt((double)D);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * NWV), 0, st, q, ksw, nqb, nkb, scale, p, counts, bitmask, nkw,
-                     head_load, bsum, BH, sel, status);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * NWV), 0, st, a, r.BH);
   FV_CHECK_LAUNCH();
   return FVATTN_OK;
+}
+
+template <typename T, int D, int MT, int NWV>
+static int launch_route_mt(const RouteLaunch &r, hipStream_t st) {
+  const SelOpts &sel = r.sel;
+  const bool ext = sel.mode != FVATTN_ROUTE_TOPP || sel.k_min > 1 || sel.k_max > 0 || sel.window > 0 ||
+                   sel.imp != nullptr;
+  return ext ? launch_route_k<T, D, MT, NWV, true>(r, st) : launch_route_k<T, D, MT, NWV, false>(r, st);
 }
 
 // Key tiles (of 16 blocks) per wave: up to 512 key blocks run on 4 waves with at most 8 tiles
 // each; more on 8 waves with 8 tiles each (up to 1024) or 10 (up to 1280).
 template <typename T, int D>
-static int launch_select_d(const void *q, const double *ksw, int BH, int nqb, int nkb, double p, int32_t *counts,
-                           uint32_t *bitmask, int nkw, int32_t *head_load, int32_t *bsum, const SelOpts &sel,
-                           uint32_t *status, hipStream_t st) {
-  const int nkt = cdiv(nkb, 16);
-#define FV_SEL(MT, NWV) \
-  return launch_select_mt<T, D, MT, NWV>(q, ksw, BH, nqb, nkb, p, counts, bitmask, nkw, head_load, bsum, sel, status, \
-                                         st)
-  if (nkt <= 4) FV_SEL(1, 4);
-  if (nkt <= 8) FV_SEL(2, 4);
-  if (nkt <= 16) FV_SEL(4, 4);
-  if (nkt <= 32) FV_SEL(8, 4);
-  if (nkt <= 64) FV_SEL(8, 8);
-  FV_SEL(10, 8);
-#undef FV_SEL
+static int launch_route_d(const RouteLaunch &r, hipStream_t st) {
+  const int nkt = cdiv(r.nkb, 16);
+  if (nkt <= 4) return launch_route_mt<T, D, 1, 4>(r, st);
+  if (nkt <= 8) return launch_route_mt<T, D, 2, 4>(r, st);
+  if (nkt <= 16) return launch_route_mt<T, D, 4, 4>(r, st);
+  if (nkt <= 32) return launch_route_mt<T, D, 8, 4>(r, st);
+  if (nkt <= 64) return launch_route_mt<T, D, 8, 8>(r, st);
+  return launch_route_mt<T, D, 10, 8>(r, st);
 }
 
-int launch_select(const void *q, const double *ksw, int BH, int d, int dtype, int nqb, int nkb, double p,
-                  int32_t *counts, uint32_t *bitmask, int nkw, int32_t *head_load, int32_t *bsum, int mode, int topk,
-                  int k_min, int k_max, int window, int bq, int bk, int N, double *imp, uint32_t *status,
-                  hipStream_t st) {
-  const SelOpts sel{mode, topk, k_min, k_max, window, bq, bk, N, imp};
-  if (dtype == FVATTN_BF16) {
-    if (d == 128)
-      return launch_select_d<uint16_t, 128>(q, ksw, BH, nqb, nkb, p, counts, bitmask, nkw, head_load, bsum, sel, status, st);
-    return launch_select_d<uint16_t, 64>(q, ksw, BH, nqb, nkb, p, counts, bitmask, nkw, head_load, bsum, sel, status, st);
-  }
-  if (d == 128)
-    return launch_select_d<float, 128>(q, ksw, BH, nqb, nkb, p, counts, bitmask, nkw, head_load, bsum, sel, status, st);
-  return launch_select_d<float, 64>(q, ksw, BH, nqb, nkb, p, counts, bitmask, nkw, head_load, bsum, sel, status, st);
+int launch_route(const RouteLaunch &r, hipStream_t st) {
+  if (r.dtype == FVATTN_BF16) return r.d == 128 ? launch_route_d<uint16_t, 128>(r, st) : launch_route_d<uint16_t, 64>(r, st);
+  return r.d == 128 ? launch_route_d<float, 128>(r, st) : launch_route_d<float, 64>(r, st);
 }
 
 int launch_csr(const int32_t *counts, const uint32_t *bitmask, const int32_t *bsum, int rows, int nkw, int nkb,
