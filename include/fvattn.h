@@ -14,7 +14,8 @@
  *    d fastest), the layout of the tutorial's block-sparse function (section 5.2).
  *  - Element type: FVATTN_BF16 (bfloat16; outputs rounded to nearest even) or FVATTN_F32.
  *  - Supported: d in {64, 128}; block_q in {32, 64, 128}; block_k in {32, 64};
- *    ceil(N / block_k) <= 1280.  Other values return FVATTN_ERR_UNSUPPORTED.
+ *    ceil(N / block_k) <= 4096 (262,144 tokens at 64-token key blocks).  Other values return
+ *    FVATTN_ERR_UNSUPPORTED.
  *  - Row r of the routing is (b*H + h) * nqb + i for query block i; nqb = ceil(N/block_q),
  *    nkb = ceil(N/block_k).  The last block of each kind may be short (ragged): pooling
  *    averages its real tokens only, and padding never attends or is attended to.
@@ -178,7 +179,8 @@ const char *fvattn_strerror(int code);
 /* Worst-case CSR size B*H*nqb*nkb (every block kept), or a negative error code. */
 int64_t fvattn_csr_max_nnz(int B, int H, int N, int block_q, int block_k);
 
-/* Bytes of workspace fvattn_route needs (0 on invalid arguments). */
+/* Bytes of workspace fvattn_route needs (0 on invalid arguments).  Above 1024 key blocks it holds a
+   score scratch of 256 x 16 rows x nkb doubles (up to 134 MB at 4096 key blocks). */
 size_t fvattn_route_ws_bytes(int B, int H, int N, int d, int block_q, int block_k);
 
 /* Bytes of workspace fvattn_sparse_attn needs (0 on invalid arguments). */

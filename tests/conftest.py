@@ -23,7 +23,7 @@ def pytest_terminal_summary(terminalreporter, exitstatus, config):
     tr = terminalreporter
     tr.section("parity records")
     keys = ("rows", "exact", "excused_A", "neartie_B", "fail", "kept_frac", "attn_rows", "attn_max_abs",
-            "attn_mean_abs", "bf16_max_abs", "bf16_mean_abs", "bf16_max_abs_beyond_rounding", "max_abs", "mean_abs", "status")
+            "attn_mean_abs", "bf16_max_abs", "bf16_mean_abs", "bf16_max_abs_beyond_rounding", "bf16_mean_abs_beyond_rounding", "max_abs", "mean_abs", "status")
     tot = dict(rows=0, exact=0, excused_A=0, neartie_B=0, fail=0)
     for name, pl in RECORDS:
         if "exact" in pl and "rows" in pl:

@@ -92,7 +92,7 @@ def test_route_rejects_bad_p(L, p):
     (dict(d=96), UNSUPPORTED), (dict(d=256), UNSUPPORTED), (dict(bq=48), UNSUPPORTED),
     (dict(bk=128), UNSUPPORTED), (dict(dt=5), UNSUPPORTED), (dict(B=0), INVALID), (dict(H=-1), INVALID),
     (dict(N=0), INVALID), (dict(q=None), INVALID), (dict(k=None), INVALID), (dict(ws=None), INVALID),
-    (dict(csr=False), INVALID), (dict(N=81921, bk=64), UNSUPPORTED), (dict(N=40961, bk=32), UNSUPPORTED),
+    (dict(csr=False), INVALID), (dict(N=262145, bk=64), UNSUPPORTED), (dict(N=131073, bk=32), UNSUPPORTED),
 ])
 def test_route_validation(L, kw, code):
     assert _route(L, **kw) == code

@@ -326,7 +326,17 @@ def test_determinism_schedule_independence_and_trace():
 
 # ------------------------------------------------------------------ full-size workloads
 FULL = [("wan1p3b_n32760", 0.9), ("wan14b_n32760", 0.90), ("wan14b_n32760", 0.95), ("wan14b_n32760", 1.0),
-        ("wan14b_n32760_bk32", 0.9), ("wan14b_n75600", 0.9), ("skew_n75600_bq128", 0.95)]
+        ("wan14b_n32760_bk32", 0.9), ("wan14b_n75600", 0.9), ("wan14b_n75600_bk32", 0.9),
+        ("skew_n75600_bq128", 0.95),
+        # single heads of 102,400 and 131,040 tokens (1600 and 4095 key blocks)
+        ("long_h1_n102400", 0.9), ("long_h1_n131040_bk32", 0.9)]
+
+LONG = {
+    "long_h1_n102400": lambda: workloads.small_case(1, 102400, 128, 64, 64, 81, ("uniform", 0.0, 3.0), "bf16",
+                                                    (32, 40, 80)),
+    "long_h1_n131040_bk32": lambda: workloads.small_case(1, 131040, 128, 64, 32, 82, ("uniform", 0.0, 3.0), "bf16",
+                                                         (39, 40, 84)),
+}
 
 
 @pytest.mark.parametrize("name,p", FULL, ids=[f"{n}_p{p}" for n, p in FULL])
@@ -335,7 +345,7 @@ def test_full_size(name, p):
     and every CSR row is compared; attention is compared on the heaviest row, the lightest row,
     the ragged last query block and one random block of every head, for the float32 output and
     for the bf16 output (which must also be the round-to-nearest-even of the float32 output)."""
-    w = workloads.get(name)
+    w = LONG[name]() if name in LONG else workloads.get(name)
     say(f"full {name} p={p}: generating inputs")
     q, k, v = workloads.make_qkv(w)
     qd, kd, vd = to_dev(q, w.dtype), to_dev(k, w.dtype), to_dev(v, w.dtype)
@@ -376,11 +386,13 @@ def test_full_size(name, p):
                                      head_load_max_over_mean=float(hl.max() / hl.mean()), attn_rows=nrows_att,
                                      attn_max_abs=float(err32.max()), attn_mean_abs=float(err32.mean()),
                                      bf16_max_abs=float(err16.max()), bf16_mean_abs=float(err16.mean()),
-                                     bf16_max_abs_beyond_rounding=float(err16x.max()), **res))
+                                     bf16_max_abs_beyond_rounding=float(err16x.max()),
+                                     bf16_mean_abs_beyond_rounding=float(np.maximum(err16x, 0.0).mean()), **res))
     assert res["fail"] == 0, res["fail_rows"]
     assert res["exact"] + res["excused_A"] + res["neartie_B"] == w.rows
     assert err32.max() <= BF16_MAX_ABS and err32.mean() <= BF16_MEAN_ABS
-    # bf16 output: the mean bound as stated; the max bound beyond the half ulp that rounding the exact
-    # result to bf16 itself leaves (one bf16 ulp is 2^-4 for |o| in [8, 16), above the 2e-2 bound)
-    assert err16.mean() <= BF16_MEAN_ABS
+    # bf16 output: both bounds on the error beyond the half ulp that rounding the exact result to
+    # bf16 itself leaves (one bf16 ulp is 2^-6 for |o| in [2, 4) and 2^-4 in [8, 16), so the raw
+    # bf16 error of any correct output can exceed the stated bounds); the raw figures are recorded
     assert err16x.max() <= BF16_MAX_ABS
+    assert np.maximum(err16x, 0.0).mean() <= BF16_MEAN_ABS

@@ -120,6 +120,9 @@ CASES = [
                                                       (4, 10, 25)), 0.8),
     ("bf16_h2_n22050_bk32_nkb690", lambda: workloads.small_case(2, 22050, 128, 64, 32, 54, ("uniform", 0.0, 3.5),
                                                                 "bf16", (21, 30, 35)), 0.85),
+    ("bf16_h2_n69120_bq128_bk32_nkb2160", lambda: workloads.small_case(2, 69120, 128, 128, 32, 55,
+                                                                       ("uniform", 0.5, 3.0), "bf16",
+                                                                       (24, 36, 80)), 0.9),
 ]
 SETTINGS = [
     ("g2_a0.5", dict(groups=2, alpha=0.5, tau=0.0), {}),

@@ -57,6 +57,8 @@ CASES = [
                                                                 "bf16", (21, 30, 35))),
     ("bf16_h1_n75600_nkb1182", lambda: workloads.small_case(1, 75600, 128, 64, 64, 45, ("uniform", 0.0, 3.0),
                                                             "bf16", (21, 45, 80))),
+    ("bf16_h1_n69120_bk32_nkb2160", lambda: workloads.small_case(1, 69120, 128, 64, 32, 47, ("uniform", 0.0, 3.0),
+                                                                 "bf16", (24, 36, 80))),
 ]
 
 VARIANTS = [

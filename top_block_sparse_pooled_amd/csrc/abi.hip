@@ -32,7 +32,7 @@ int launch_attn_f32(const void *q, const void *k, const void *v, void *o, const 
 
 namespace {
 
-constexpr int kMaxNkb = 1280;
+constexpr int kMaxNkb = 4096;
 constexpr int kMaxBH = 65535;
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -67,6 +67,7 @@ struct RouteWs {
   int32_t *counts;
   uint32_t *bitmask;
   int32_t *bsum;   // per-64-row sums of counts
+  double *scr;     // score scratch of the large select (more than 1024 key blocks), else null
   int nblk;
   size_t bytes;
 };
@@ -85,6 +86,11 @@ RouteWs route_ws_layout(const Shape &s, char *base) {
   w.nblk = (s.rows + 63) / 64;
   w.bsum = (int32_t *)(base + off);
   off += align256((size_t)w.nblk * sizeof(int32_t));
+  w.scr = nullptr;
+  if (s.nkb >= fv::kLargeSelMinNkb) {
+    w.scr = (double *)(base + off);
+    off += align256((size_t)fv::kLargeSelGrid * 16 * s.nkbp * sizeof(double));
+  }
   w.bytes = off;
   return w;
 }
@@ -231,6 +237,8 @@ int route_core(const void *q, const void *k, const Shape &s, int N, int d, int d
   r.nbsum = w.nblk;
   r.sel = fv::SelOpts{o.mode, o.topk, o.k_min, o.k_max, o.window, block_q, block_k, N, imp};
   r.status = w.status;
+  r.scr = w.scr;
+  r.nkbp = s.nkbp;
   if ((rc = fv::launch_route(r, st)) != FVATTN_OK) return rc;
   if (!csr_after) return FVATTN_OK;
   return fv::launch_csr(w.counts, w.bitmask, w.bsum, s.rows, s.nkw, s.nkb, csr->row_ptr, csr->col_idx, st);

@@ -120,7 +120,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_pp(
   constexpr int PB = 64 / BK;     // key blocks per tile
   constexpr int G = 128 / BQ;     // query blocks per unit
   constexpr int WPQ = BQ / 32;    // waves per query block (within a group)
-  constexpr int MAXW = 40;        // kept-block bitmap words (1280 key blocks)
+  constexpr int MAXW = 128;       // kept-block bitmap words (4096 key blocks)
   constexpr int NTH = 512;
   constexpr int NH = C::NM / 2;   // 32-dim output tiles finalised by each group
   __shared__ __attribute__((aligned(1024))) uint8_t K0[2][C::KBYTES];   // [group]; parity 0
@@ -297,16 +297,19 @@ __global__ __launch_bounds__(512, 1) void k_attn_pp(
     if (w == 0) {
       int base = 0;
       for (int c = 0; c < NCLS; ++c) {
-        const uint32_t word = lane < nkw ? class_word(c, lane) : 0u;
-        const int pc = __popc(word);
-        int incl = pc;
+        for (int w0 = 0; w0 < nkw; w0 += 64) {   // 64 words at a time
+          const int x = w0 + lane;
+          const uint32_t word = x < nkw ? class_word(c, x) : 0u;
+          const int pc = __popc(word);
+          int incl = pc;
 #pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          const int ov = __shfl_up(incl, off);
-          if (lane >= off) incl += ov;
+          for (int off = 1; off < 64; off <<= 1) {
+            const int ov = __shfl_up(incl, off);
+            if (lane >= off) incl += ov;
+          }
+          if (x < MAXW) s_cpre[c][x] = base + incl - pc;
+          base += __shfl(incl, 63);
         }
-        if (lane < MAXW) s_cpre[c][lane] = base + incl - pc;
-        base += __shfl(incl, 63);
       }
       if (lane == 0) s_n = base;
     }

@@ -165,7 +165,9 @@ __global__ __launch_bounds__(256) void k_pool(PoolArgs a) {
 //      ballots.  No workgroup barrier inside the selection.
 // Outputs counts[row] and the kept-bit mask bitmask[row][nkw]; adds loads to head_load.
 // ---------------------------------------------------------------------------------------
-constexpr int kMaxNkw = 40;  // 1280 key blocks
+// Kept-bit words of a row: word wi (key blocks 32 wi .. 32 wi + 31) is held by lane wi % 64 in
+// its register wi / 64; two registers cover 4096 key blocks.
+constexpr int kRowWords = 2;
 
 constexpr double kFix52 = 4503599627370496.0;  // 2^52: masses as fixed point
 
@@ -179,11 +181,26 @@ constexpr double kFix52 = 4503599627370496.0;  // 2^52: masses as fixed point
 // the bin holds one key or one key value (ties, resolved toward lower indices).  Returns the
 // kept-bit word of key blocks 32 lane .. 32 lane + 31 (zero for lanes past the row) and sets
 // `count` to the number of kept blocks.
+// A row of softmax numerators (lane l: key block l + 64 t): in registers, or in memory (the
+// large select's scratch), read once per pass.
 template <int NPL>
-__device__ __forceinline__ uint32_t select_row(const double (&ev)[NPL], int nkb, bool bycnt, unsigned long long T,
-                                               unsigned long long lo0, bool keep_all,
-                                               unsigned long long *__restrict__ hm, uint32_t *__restrict__ hc,
-                                               uint32_t *__restrict__ status, int &count) {
+struct RegRow {
+  static constexpr int kUnroll = NPL;
+  const double (&v)[NPL];
+  __device__ __forceinline__ double get(int t) const { return v[t]; }
+};
+struct MemRow {
+  static constexpr int kUnroll = 4;
+  const double *p;
+  __device__ __forceinline__ double get(int t) const { return p[(threadIdx.x & 63) + 64 * t]; }
+};
+
+template <int NPL, class Row>
+__device__ __forceinline__ void select_row(const Row &ev, int nkb, bool bycnt, unsigned long long T,
+                                           unsigned long long lo0, bool keep_all,
+                                           unsigned long long *__restrict__ hm, uint32_t *__restrict__ hc,
+                                           uint32_t *__restrict__ status, uint32_t (&words)[kRowWords], int &count) {
+  static_assert(NPL <= 32 * kRowWords, "row longer than the kept-word registers");
   const int lane = threadIdx.x & 63;
   unsigned long long lo = lo0;
   unsigned long long width = (unsigned long long)__double_as_longlong(1.0) + 1ull - lo0;
@@ -200,13 +217,15 @@ __device__ __forceinline__ uint32_t select_row(const double (&ev)[NPL], int nkb,
     // (LDS operations of one wave take effect in issue order; the fences only keep the
     // compiler from moving them)
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-#pragma unroll
+#pragma unroll Row::kUnroll
     for (int t = 0; t < NPL; ++t) {
-      const unsigned long long off = (unsigned long long)__double_as_longlong(ev[t]) - lo;
-      if (lane + 64 * t < nkb && off < width) {
+      const bool valid = lane + 64 * t < nkb;
+      const double e = valid ? ev.get(t) : 0.0;   // entries past the row are never read
+      const unsigned long long off = (unsigned long long)__double_as_longlong(e) - lo;
+      if (valid && off < width) {
         const int dg = (int)(off >> sh);
         atomicAdd(&hc[dg], 1u);
-        if (!bycnt) atomicAdd(&hm[dg], (unsigned long long)(ev[t] * kFix52));
+        if (!bycnt) atomicAdd(&hm[dg], (unsigned long long)(e * kFix52));
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -264,12 +283,13 @@ __device__ __forceinline__ uint32_t select_row(const double (&ev)[NPL], int nkb,
     else need = mt == 0 ? ntie : (uint32_t)min((unsigned long long)ntie, (rem + mt - 1) / mt);
   }
   uint32_t cum = 0;   // ties taken so far (ascending key block)
-  uint32_t word = 0;
-  count = 0;
 #pragma unroll
+  for (int q = 0; q < kRowWords; ++q) words[q] = 0u;
+  count = 0;
+#pragma unroll Row::kUnroll
   for (int t = 0; t < NPL; ++t) {
     const bool valid = lane + 64 * t < nkb;
-    const unsigned long long key = (unsigned long long)__double_as_longlong(ev[t]);
+    const unsigned long long key = valid ? (unsigned long long)__double_as_longlong(ev.get(t)) : 0ull;
     bool keep = valid && (st == 3 || key >= hi || (st == 1 && key >= lo));
     if (st == 2) {
       const bool tie = valid && key == lo;
@@ -279,11 +299,11 @@ __device__ __forceinline__ uint32_t select_row(const double (&ev)[NPL], int nkb,
       cum += (uint32_t)__popcll(bt);
     }
     const unsigned long long mt = __ballot(keep);
-    if (lane == 2 * t) word = (uint32_t)mt;
-    if (lane == 2 * t + 1) word = (uint32_t)(mt >> 32);
+    // key blocks 64 t .. 64 t + 63 are words 2 t and 2 t + 1
+    if (lane == (2 * t) % 64) words[(2 * t) / 64] = (uint32_t)mt;
+    if (lane == (2 * t + 1) % 64) words[(2 * t + 1) / 64] = (uint32_t)(mt >> 32);
     count += (int)__popcll(mt);
   }
-  return word;
 }
 
 // Arguments of one select item.
@@ -298,6 +318,77 @@ struct SelArgs {
   SelOpts sel;
   uint32_t *status;
 };
+
+// The kept set of one row from its softmax numerators ev (lane l: key block l + 64 t), their
+// fixed-point sum Z and minimum emin: the Top-p cut (or a routing variant), the kept-bit words
+// written to bitmask, the count to counts and *cnt_out (lane 0), and for SASA the importance of
+// every block.  hm / hc: the wave's radix histograms.
+template <int NPL, bool EXT, class Row>
+__device__ __forceinline__ void row_decide(const Row &ev, unsigned long long Z, double emin, int i,
+                                           size_t row, const SelArgs &a, unsigned long long *__restrict__ hm,
+                                           uint32_t *__restrict__ hc, int *cnt_out) {
+  const int lane = threadIdx.x & 63;
+  const int nkb = a.nkb, nkw = a.nkw;
+  const unsigned long long lo0 = (unsigned long long)__double_as_longlong(emin);
+  // search by mass (Top-p) or by count (top-k, or a clamped Top-p count)
+  bool bycnt = false;
+  unsigned long long tgt0;
+  bool all;
+  if (EXT && a.sel.mode == FVATTN_ROUTE_TOPK) {
+    bycnt = true;
+    tgt0 = (unsigned long long)a.sel.topk;
+    all = a.sel.topk >= nkb;
+  } else {
+    tgt0 = (unsigned long long)ceil(a.p * (double)Z);
+    if (tgt0 > Z) tgt0 = Z;
+    if (tgt0 < 1) tgt0 = 1;
+    all = a.p >= 1.0;
+  }
+  int c;
+  uint32_t words[kRowWords];
+  select_row<NPL>(ev, nkb, bycnt, tgt0, lo0, all, hm, hc, a.status, words, c);
+  if (EXT && !bycnt && (a.sel.k_min > 1 || a.sel.k_max > 0)) {
+    // clamp of the Top-p count: re-select by count when it lies outside [k_min, k_max]
+    int tgt = max(c, a.sel.k_min);
+    if (a.sel.k_max > 0) tgt = min(tgt, a.sel.k_max);
+    tgt = min(tgt, nkb);
+    if (tgt != c)
+      select_row<NPL>(ev, nkb, true, (unsigned long long)tgt, lo0, tgt >= nkb, hm, hc, a.status,
+                      words, c);
+  }
+  if (EXT && a.sel.window > 0) {
+    // local window: key blocks within `window` of those overlapping the query block's tokens
+    const int t0 = i * a.sel.bq, t1 = min(t0 + a.sel.bq, a.sel.N) - 1;
+    const int ja = max(0, t0 / a.sel.bk - a.sel.window), jb = min(nkb - 1, t1 / a.sel.bk + a.sel.window);
+    c = 0;
+#pragma unroll
+    for (int q = 0; q < kRowWords; ++q) {
+      const int wi = lane + 64 * q;
+      const int lo_j = max(ja, 32 * wi), hi_j = min(jb, 32 * wi + 31);
+      if (wi < nkw && lo_j <= hi_j) {
+        const int nbits = hi_j - lo_j + 1;
+        words[q] |= (nbits == 32 ? 0xffffffffu : ((1u << nbits) - 1u)) << (lo_j - 32 * wi);
+      }
+      c += __popc(words[q]);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) c += __shfl_xor(c, off);
+  }
+#pragma unroll
+  for (int q = 0; q < kRowWords; ++q)
+    if (lane + 64 * q < nkw) a.bitmask[row * nkw + lane + 64 * q] = words[q];
+  if (lane == 0) {
+    a.counts[row] = c;
+    *cnt_out = c;
+  }
+  if (EXT && a.sel.imp != nullptr) {
+    // importance of every block: the candidates' order for SASA
+    const double invz = Z > 0 ? kFix52 / (double)Z : 0.0;   // 1 / Z with Z in 2^-52 units
+#pragma unroll Row::kUnroll
+    for (int t = 0; t < NPL; ++t)
+      if (lane + 64 * t < nkb) a.sel.imp[row * nkb + lane + 64 * t] = ev.get(t) * invz;
+  }
+}
 
 // LDS of a select workgroup: NWV waves, MAXT key tiles of 16 per wave.
 template <typename T, int D, int MAXT, int NWV>
@@ -491,60 +582,7 @@ __device__ __forceinline__ void select_item(SelLds<T, D, MAXT, NWV> &L, const Se
         Z += L.zpart[ww][r];
         emin = fmin(emin, L.minpart[ww][r]);
       }
-      const unsigned long long lo0 = (unsigned long long)__double_as_longlong(emin);
-      // search by mass (Top-p) or by count (top-k, or a clamped Top-p count)
-      bool bycnt = false;
-      unsigned long long tgt0;
-      bool all;
-      if (EXT && a.sel.mode == FVATTN_ROUTE_TOPK) {
-        bycnt = true;
-        tgt0 = (unsigned long long)a.sel.topk;
-        all = a.sel.topk >= nkb;
-      } else {
-        tgt0 = (unsigned long long)ceil(a.p * (double)Z);
-        if (tgt0 > Z) tgt0 = Z;
-        if (tgt0 < 1) tgt0 = 1;
-        all = a.p >= 1.0;
-      }
-      int c;
-      // lane L < nkw holds kept word L (key blocks 32 L .. 32 L + 31)
-      uint32_t word = select_row<NPL>(ev, nkb, bycnt, tgt0, lo0, all, L.h_mass[w], L.h_cnt[w], a.status, c);
-      if (EXT && !bycnt && (a.sel.k_min > 1 || a.sel.k_max > 0)) {
-        // clamp of the Top-p count: re-select by count when it lies outside [k_min, k_max]
-        int tgt = max(c, a.sel.k_min);
-        if (a.sel.k_max > 0) tgt = min(tgt, a.sel.k_max);
-        tgt = min(tgt, nkb);
-        if (tgt != c)
-          word = select_row<NPL>(ev, nkb, true, (unsigned long long)tgt, lo0, tgt >= nkb, L.h_mass[w], L.h_cnt[w], a.status,
-                                 c);
-      }
-      if (EXT && a.sel.window > 0 && lane < nkw) {
-        // local window: key blocks within `window` of those overlapping the query block's tokens
-        const int t0 = i * a.sel.bq, t1 = min(t0 + a.sel.bq, a.sel.N) - 1;
-        const int ja = max(0, t0 / a.sel.bk - a.sel.window), jb = min(nkb - 1, t1 / a.sel.bk + a.sel.window);
-        const int lo_j = max(ja, 32 * lane), hi_j = min(jb, 32 * lane + 31);
-        if (lo_j <= hi_j) {
-          const int nbits = hi_j - lo_j + 1;
-          word |= (nbits == 32 ? 0xffffffffu : ((1u << nbits) - 1u)) << (lo_j - 32 * lane);
-        }
-      }
-      if (EXT && a.sel.window > 0) {
-        c = __popc(word);
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) c += __shfl_xor(c, off);
-      }
-      if (lane < nkw) a.bitmask[row * nkw + lane] = word;
-      if (lane == 0) {
-        a.counts[row] = c;
-        L.cnt[r] = c;
-      }
-      if (EXT && a.sel.imp != nullptr) {
-        // importance of every block: the candidates' order for SASA
-        const double invz = Z > 0 ? kFix52 / (double)Z : 0.0;   // 1 / Z with Z in 2^-52 units
-#pragma unroll
-        for (int t = 0; t < NPL; ++t)
-          if (lane + 64 * t < nkb) a.sel.imp[row * nkb + lane + 64 * t] = ev[t] * invz;
-      }
+      row_decide<NPL, EXT>(RegRow<NPL>{ev}, Z, emin, i, row, a, L.h_mass[w], L.h_cnt[w], &L.cnt[r]);
     }
     __syncthreads();   // staged rows and partial sums consumed before they are overwritten
   }
@@ -585,6 +623,160 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 ? 2 : 1) void k_select(SelArgs a
   }
 }
 
+
+// ---------------------------------------------------------------------------------------
+// Select for more than 1024 key blocks (up to 4096): 8 waves; the scores of an item's 16 rows are
+// computed in chunks of 1024 key blocks (8 tiles of 16 per wave, the same float64 MFMA sequence
+// as the select above) and stored, scaled, to a scratch of 16 rows owned by the workgroup; each
+// wave then takes whole rows: row maximum, e = exp(s - max) written back in place, fixed-point Z
+// and minimum of e by wave reductions (the same values as the select above), and the radix
+// selection reading the row from the scratch (L2-resident) in each pass.
+// ---------------------------------------------------------------------------------------
+template <typename T, int D>
+struct SelLdsL {
+  double eq[16 * D];   // the item's pooled query blocks (float64 MFMA operand order)
+  unsigned long long h_mass[8][256];
+  uint32_t h_cnt[8][256];
+  int cnt[16];
+};
+
+template <typename T, int D, int NPL, bool EXT>
+__device__ __forceinline__ void select_item_large(SelLdsL<T, D> &L, const SelArgs &a, double *__restrict__ scr,
+                                                  int nkbp, int bh, int g) {
+  constexpr int NWV = 8, MAXT = 8, KS = D / 4;
+  constexpr int EPC = DT<T>::per16, CPR = D / EPC;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nqb = a.nqb, nkb = a.nkb;
+  const int nkt = (nkb + 15) >> 4;
+  {
+    const T *xh = reinterpret_cast<const T *>(a.qraw) + (size_t)bh * a.sel.N * D;
+    for (int jj = w; jj < 16; jj += NWV) {
+      double m[1][EPC];
+      pool_blocks<T, D, 1>(xh, 16 * g + jj, NWV, a.sel.bq, nqb, a.sel.N, m);
+      if (lane < CPR) {
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) {
+          const int cc = lane * EPC + e;
+          L.eq[(cc >> 2) * 64 + jj + 16 * (cc & 3)] = m[0][e];
+        }
+      }
+    }
+  }
+  __syncthreads();
+  const int jl = lane & 15, ig = lane >> 4;
+  const double *qa = L.eq + lane;
+  for (int c0 = 0; c0 < nkt; c0 += NWV * MAXT) {
+    d4 acc[MAXT];
+#pragma unroll
+    for (int k = 0; k < MAXT; ++k) acc[k] = d4{0.0, 0.0, 0.0, 0.0};
+    const double *kb[MAXT];
+#pragma unroll
+    for (int k = 0; k < MAXT; ++k)
+      kb[k] = a.ksw + ((size_t)(bh * nkt + min(c0 + w + NWV * k, nkt - 1)) * KS) * 64 + lane;
+    double abuf = qa[0], bbuf[MAXT];
+#pragma unroll
+    for (int k = 0; k < MAXT; ++k) bbuf[k] = kb[k][0];
+    // k-steps in a rolled loop (an unrolled one lets the scheduler hoist the operand loads of
+    // many steps and spill at d = 128)
+#pragma unroll 2
+    for (int s = 0; s < KS; ++s) {
+      const double av = abuf;
+      double b[MAXT];
+#pragma unroll
+      for (int k = 0; k < MAXT; ++k) b[k] = bbuf[k];
+      if (s + 1 < KS) {
+        abuf = qa[(s + 1) * 64];
+#pragma unroll
+        for (int k = 0; k < MAXT; ++k) bbuf[k] = kb[k][(s + 1) * 64];
+      }
+#pragma unroll
+      for (int k = 0; k < MAXT; ++k) acc[k] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, b[k], acc[k], 0, 0, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < MAXT; ++k) {
+      const int tile = c0 + w + NWV * k;
+      if (tile < nkt) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          acc[k][v] *= a.scale;
+          scr[(size_t)(ig + 4 * v) * nkbp + 16 * tile + jl] = acc[k][v];
+        }
+      }
+    }
+  }
+  __syncthreads();   // every wave's scores stored and visible to the workgroup
+  for (int rr = 0; rr < 16 / NWV; ++rr) {
+    const int r = w + NWV * rr, i = 16 * g + r;
+    if (i >= nqb) {   // wave-uniform
+      if (lane == 0) L.cnt[r] = 0;
+      continue;
+    }
+    const size_t row = (size_t)bh * nqb + i;
+    double *sr = scr + (size_t)r * nkbp;   // this lane reads and writes entries lane + 64 t only
+    double mx = -INFINITY;
+#pragma unroll 2
+    for (int t = 0; t < NPL; ++t) {
+      const int j = lane + 64 * t;
+      if (j < nkb) mx = fmax(mx, sr[j]);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mx = fmax(mx, __shfl_xor(mx, off));
+    unsigned long long Z = 0;
+    double emin = 1.0;
+#pragma unroll 2
+    for (int t = 0; t < NPL; ++t) {
+      const int j = lane + 64 * t;
+      if (j < nkb) {
+        const double e = exp(sr[j] - mx);
+        sr[j] = e;
+        Z += (unsigned long long)(e * kFix52);
+        emin = fmin(emin, e);
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      Z += __shfl_xor(Z, off);
+      emin = fmin(emin, __shfl_xor(emin, off));
+    }
+    row_decide<NPL, EXT>(MemRow{sr}, Z, emin, i, row, a, L.h_mass[w], L.h_cnt[w], &L.cnt[r]);
+  }
+  __syncthreads();   // row counts in LDS; scratch rows consumed before the next item's scores
+  if (w == 0) {
+    const size_t row0 = (size_t)bh * nqb + 16 * g;
+    const int c = lane < 16 ? L.cnt[lane] : 0;
+    const bool second = lane < 16 && ((row0 + lane) >> 6) != (row0 >> 6);
+    int c0 = second ? 0 : c, c1 = second ? c : 0;
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) {
+      c0 += __shfl_xor(c0, off);
+      c1 += __shfl_xor(c1, off);
+    }
+    if (lane == 0) {
+      atomicAdd(&a.head_load[bh], c0 + c1);
+      atomicAdd(&a.bsum[row0 >> 6], c0);
+      if (c1 != 0) atomicAdd(&a.bsum[(row0 >> 6) + 1], c1);
+    }
+  }
+}
+
+// Persistent large select: items split into 8 XCD ranges as k_select; workgroup b owns scratch
+// rows scr + 16 b nkbp (gridDim.x <= kLargeSelGrid).
+template <typename T, int D, int NPL, bool EXT>
+__global__ __launch_bounds__(512, 1) void k_select_large(SelArgs a, int BH, double *scr, int nkbp) {
+  __shared__ SelLdsL<T, D> L;
+  const int nqg = (a.nqb + 15) >> 4;
+  const int items = BH * nqg;
+  const int xcd = blockIdx.x & 7;
+  const int nwx = ((int)gridDim.x - xcd + 7) >> 3;
+  const int it_end = (int)((long long)items * (xcd + 1) / 8);
+  double *my = scr + (size_t)blockIdx.x * 16 * nkbp;
+  for (int it = (int)((long long)items * xcd / 8) + (int)(blockIdx.x >> 3); it < it_end; it += nwx) {
+    const int bh = it / nqg, g = it - bh * nqg;
+    select_item_large<T, D, NPL, EXT>(L, a, my, nkbp, bh, g);
+  }
+}
+
 // ---------------------------------------------------------------------------------------
 // k_csr: row_ptr (exclusive scan of counts) and ascending col_idx from the kept masks.
 // grid = cdiv(rows, 16), 256 threads; wave w owns rows 16 b + 4 w .. + 3, with no workgroup
@@ -592,7 +784,8 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 ? 2 : 1) void k_select(SelArgs a
 // counts of the rows before it inside that block (an exclusive scan across the lanes).  Lane L
 // holds word L of a row's mask (the four rows' words are loaded up front), and each 64-block
 // chunk of a row is one 64-bit mask from two lanes, whose set bits give every kept block its
-// output slot (coalesced writes).
+// output slot (coalesced writes).  Rows of up to 128 words (4096 key blocks): lane L holds words
+// L and L + 64.
 // ---------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_csr(const int32_t *__restrict__ counts,
                                              const uint32_t *__restrict__ bitmask,
@@ -601,11 +794,13 @@ __global__ __launch_bounds__(256) void k_csr(const int32_t *__restrict__ counts,
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int r0 = blockIdx.x * 16 + 4 * w;   // this wave's first row
   if (r0 >= rows) return;                    // wave-uniform
-  uint32_t wv[4];
+  uint32_t wv[4][kRowWords];   // row k's word lane + 64 q in wv[k][q]
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int rk = r0 + k;
-    wv[k] = (rk < rows && lane < nkw) ? bitmask[(size_t)rk * nkw + lane] : 0u;
+#pragma unroll
+    for (int q = 0; q < kRowWords; ++q)
+      wv[k][q] = (rk < rows && lane + 64 * q < nkw) ? bitmask[(size_t)rk * nkw + lane + 64 * q] : 0u;
   }
   const int blk = r0 >> 6;
   const int cl = (64 * blk + lane < rows) ? counts[64 * blk + lane] : 0;
@@ -633,8 +828,11 @@ __global__ __launch_bounds__(256) void k_csr(const int32_t *__restrict__ counts,
       if (rk == rows - 1) row_ptr[rows] = out + ck;
     }
     for (int c = 0; c < nch; ++c) {
-      const unsigned long long mask = (unsigned long long)(uint32_t)__shfl((int)wv[k], 2 * c) |
-                                      ((unsigned long long)(uint32_t)__shfl((int)wv[k], 2 * c + 1) << 32);
+      // words 2 c and 2 c + 1 sit in the same register (c / 32) of lanes 2 c % 64 and 2 c % 64 + 1
+      const int src = c >> 5, l0 = (2 * c) & 63;
+      const uint32_t wq = src == 0 ? wv[k][0] : wv[k][kRowWords - 1];
+      const unsigned long long mask = (unsigned long long)(uint32_t)__shfl((int)wq, l0) |
+                                      ((unsigned long long)(uint32_t)__shfl((int)wq, l0 + 1) << 32);
       if ((mask >> lane) & 1ull) col_idx[out + __popcll(mask & lt)] = 64 * c + lane;
       out += __popcll(mask);
     }
@@ -712,6 +910,27 @@ static int launch_route_k(const RouteLaunch &r, hipStream_t st) {
   return FVATTN_OK;
 }
 
+template <typename T, int D, int NPL, bool EXT>
+static int launch_route_large(const RouteLaunch &r, hipStream_t st) {
+  const SelArgs a{r.q, r.ksw, r.nqb, r.nkb, r.nkw, 1.0 / sqrt((double)D), r.p, r.counts, r.bitmask, r.head_load,
+                  r.bsum, r.sel, r.status};
+  int rc = launch_pool_k(r.k, r.BH, r.N, D, r.dtype, r.bk, r.ksw, r.bsum, r.nbsum, r.head_load, r.BH,
+                         (int32_t *)r.status, 1, st);
+  if (rc != FVATTN_OK) return rc;
+  auto kern = k_select_large<T, D, NPL, EXT>;
+  int cus = 0, occ = 0;
+  if (device_cus(&cus) != 0) return FVATTN_ERR_HIP;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, 512, 0) != hipSuccess) return FVATTN_ERR_HIP;
+  const int items = cdiv(r.nqb, 16) * r.BH;
+  int grid = cus * (occ > 0 ? occ : 1);
+  grid = min(grid, items);
+  grid = max(grid, 8);
+  grid = min(grid, kLargeSelGrid);   // the scratch holds kLargeSelGrid workgroups' rows
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(512), 0, st, a, r.BH, r.scr, r.nkbp);
+  FV_CHECK_LAUNCH();
+  return FVATTN_OK;
+}
+
 template <typename T, int D, int MT, int NWV>
 static int launch_route_mt(const RouteLaunch &r, hipStream_t st) {
   const SelOpts &sel = r.sel;
@@ -721,7 +940,8 @@ static int launch_route_mt(const RouteLaunch &r, hipStream_t st) {
 }
 
 // Key tiles (of 16 blocks) per wave: up to 512 key blocks run on 4 waves with at most 8 tiles
-// each; more on 8 waves with 8 tiles each (up to 1024) or 10 (up to 1280).
+// each, up to 1024 on 8 waves with 8 tiles each; more on the chunked large select (rows of up to
+// 2048 or 4096 key blocks in registers).
 template <typename T, int D>
 static int launch_route_d(const RouteLaunch &r, hipStream_t st) {
   const int nkt = cdiv(r.nkb, 16);
@@ -730,7 +950,12 @@ static int launch_route_d(const RouteLaunch &r, hipStream_t st) {
   if (nkt <= 16) return launch_route_mt<T, D, 4, 4>(r, st);
   if (nkt <= 32) return launch_route_mt<T, D, 8, 4>(r, st);
   if (nkt <= 64) return launch_route_mt<T, D, 8, 8>(r, st);
-  return launch_route_mt<T, D, 10, 8>(r, st);
+  const SelOpts &sel = r.sel;
+  const bool ext = sel.mode != FVATTN_ROUTE_TOPP || sel.k_min > 1 || sel.k_max > 0 || sel.window > 0 ||
+                   sel.imp != nullptr;
+  if (r.nkb <= 2048)
+    return ext ? launch_route_large<T, D, 32, true>(r, st) : launch_route_large<T, D, 32, false>(r, st);
+  return ext ? launch_route_large<T, D, 64, true>(r, st) : launch_route_large<T, D, 64, false>(r, st);
 }
 
 int launch_route(const RouteLaunch &r, hipStream_t st) {

@@ -233,13 +233,19 @@ __global__ __launch_bounds__(256) void k_sasa_mark(const double *__restrict__ im
     const size_t row = (size_t)bh * nqb + i;
     const unsigned long long need = G.target - G.above;   // ties to take (state 2)
     unsigned long long rank = G.state == 2 ? (unsigned long long)tiepre[row] : 0ull;
-    // lane L < nkw holds word L of the row's kept mask; the chunk of key blocks 64c .. 64c+63
-    // is words 2c and 2c + 1
-    uint32_t word = lane < nkw ? bitmask[row * nkw + lane] : 0u;
-    const uint32_t word0 = word;
+    // lane L holds words L and L + 64 of the row's kept mask (up to 4096 key blocks); the chunk
+    // of key blocks 64c .. 64c+63 is words 2c and 2c + 1, in register c / 32 of lanes 2c % 64 and
+    // 2c % 64 + 1
+    uint32_t word[2], word0[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      word[q] = lane + 64 * q < nkw ? bitmask[row * nkw + lane + 64 * q] : 0u;
+      word0[q] = word[q];
+    }
     for (int j0 = 0; j0 < nkb; j0 += 64) {
       const int j = j0 + lane;
-      const uint32_t src = (uint32_t)__shfl((int)word0, j >> 5);
+      const int q = j0 >> 11, wl = (j0 >> 5) & 63;   // register and first lane of this chunk
+      const uint32_t src = (uint32_t)__shfl((int)(q ? word0[1] : word0[0]), wl + (lane >> 5));
       const bool kept = (src >> (j & 31)) & 1u;
       bool add = false, tie = false;
       if (j < nkb && !kept) {
@@ -259,10 +265,12 @@ __global__ __launch_bounds__(256) void k_sasa_mark(const double *__restrict__ im
       }
       const unsigned long long ab = __ballot(add);
       added += __popcll(ab);
-      if (lane == (j0 >> 5)) word |= (uint32_t)ab;
-      if (lane == (j0 >> 5) + 1) word |= (uint32_t)(ab >> 32);
+      if (lane == wl) word[q] |= (uint32_t)ab;
+      if (lane == wl + 1) word[q] |= (uint32_t)(ab >> 32);
     }
-    if (lane < nkw && word != word0) bitmask[row * nkw + lane] = word;
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      if (lane + 64 * q < nkw && word[q] != word0[q]) bitmask[row * nkw + lane + 64 * q] = word[q];
     if (lane == 0 && added > 0) counts[row] += added;
   }
   // the workgroup's four rows: one load update for the head, at most two per-64-row sums
