@@ -179,7 +179,7 @@ const char *fvattn_strerror(int code);
 /* Worst-case CSR size B*H*nqb*nkb (every block kept), or a negative error code. */
 int64_t fvattn_csr_max_nnz(int B, int H, int N, int block_q, int block_k);
 
-/* Bytes of workspace fvattn_route needs (0 on invalid arguments).  Above 1024 key blocks it holds a
+/* Bytes of workspace fvattn_route needs (0 on invalid arguments).  Above 1280 key blocks it holds a
    score scratch of 256 x 16 rows x nkb doubles (up to 134 MB at 4096 key blocks). */
 size_t fvattn_route_ws_bytes(int B, int H, int N, int d, int block_q, int block_k);
 

@@ -67,7 +67,7 @@ struct RouteWs {
   int32_t *counts;
   uint32_t *bitmask;
   int32_t *bsum;   // per-64-row sums of counts
-  double *scr;     // score scratch of the large select (more than 1024 key blocks), else null
+  double *scr;     // score scratch of the large select (more than 1280 key blocks), else null
   int nblk;
   size_t bytes;
 };

@@ -23,15 +23,15 @@ struct RouteLaunch {
   int nbsum;
   SelOpts sel;
   uint32_t *status;
-  double *scr;          // more than 1024 key blocks: kLargeSelGrid x 16 rows x nkbp scores, else unused
+  double *scr;          // more than 1280 key blocks: kLargeSelGrid x 16 rows x nkbp scores, else unused
   int nkbp;             // key blocks rounded up to 16
 };
 
-// Workgroups of the select for more than 1024 key blocks; each owns 16 rows of score scratch.
+// Workgroups of the select for more than 1280 key blocks; each owns 16 rows of score scratch.
 constexpr int kLargeSelGrid = 256;
-constexpr int kLargeSelMinNkb = 1025;
+constexpr int kLargeSelMinNkb = 1281;
 
-// Pooling of K (k_pool) and the selection (k_select, or k_select_large above 1024 key blocks).
+// Pooling of K (k_pool) and the selection (k_select, or k_select_large above 1280 key blocks).
 int launch_route(const RouteLaunch &r, hipStream_t st);
 
 }  // namespace fv
