@@ -616,9 +616,6 @@ __device__ __forceinline__ void select_item(SelLds<T, D, MAXT, NWV> &L, const Se
 // Persistent select over all items (head bh, group g of 16 query blocks).  Workgroup b runs on
 // XCD b % 8 (round-robin dispatch); XCD x owns the x-th eighth of the items in head-major
 // order, so its L2 holds the pooled keys of only a few heads.  gridDim.x >= 8.
-// Persistent select over all items (head bh, group g of 16 query blocks).  Workgroup b runs on
-// XCD b % 8 (round-robin dispatch); XCD x owns the x-th eighth of the items in head-major
-// order, so its L2 holds the pooled keys of only a few heads.  gridDim.x >= 8.
 template <typename T, int D, int MAXT, int NWV, bool EXT>
 __global__ __launch_bounds__(64 * NWV, NWV == 4 ? 2 : 1) void k_select(SelArgs a, int BH) {
   __shared__ SelLds<T, D, MAXT, NWV> L;
