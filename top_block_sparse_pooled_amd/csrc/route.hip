@@ -34,12 +34,85 @@
 namespace fv {
 
 // ---------------------------------------------------------------------------------------
+// Cross-lane steps without LDS traffic (DPP and the gfx950 lane swaps).  Only exact operations
+// (max, min, integer sums) are regrouped, and float64 sums keep their pairs, so results are the
+// same bits as with the shuffle butterflies.
+// ---------------------------------------------------------------------------------------
+template <int CTRL, int RM, int BM, bool BC>
+__device__ __forceinline__ unsigned long long dpp64(unsigned long long x) {
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)x, CTRL, RM, BM, BC);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(x >> 32), CTRL, RM, BM, BC);
+  return ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+template <int CTRL>
+__device__ __forceinline__ double dppf64(double x) {
+  return __longlong_as_double((long long)dpp64<CTRL, 0xf, 0xf, false>((unsigned long long)__double_as_longlong(x)));
+}
+// all-reduce over each row of 16 lanes: lane pairs 1 apart, 2 apart, the mirrored half-row,
+// the mirrored row
+__device__ __forceinline__ double row16_max(double x) {
+  x = fmax(x, dppf64<0xb1>(x));
+  x = fmax(x, dppf64<0x4e>(x));
+  x = fmax(x, dppf64<0x141>(x));
+  return fmax(x, dppf64<0x140>(x));
+}
+__device__ __forceinline__ double row16_min(double x) {
+  x = fmin(x, dppf64<0xb1>(x));
+  x = fmin(x, dppf64<0x4e>(x));
+  x = fmin(x, dppf64<0x141>(x));
+  return fmin(x, dppf64<0x140>(x));
+}
+__device__ __forceinline__ unsigned long long row16_sum(unsigned long long x) {
+  x += dpp64<0xb1, 0xf, 0xf, false>(x);
+  x += dpp64<0x4e, 0xf, 0xf, false>(x);
+  x += dpp64<0x141, 0xf, 0xf, false>(x);
+  return x + dpp64<0x140, 0xf, 0xf, false>(x);
+}
+// inclusive prefix sum over the 64 lanes: shifts by 1, 2, 4, 8 within rows of 16, then the
+// last lane of a row into the next row (rows 1, 3) and lane 31 into rows 2, 3
+__device__ __forceinline__ unsigned long long wave_scan(unsigned long long x) {
+  x += dpp64<0x111, 0xf, 0xf, true>(x);
+  x += dpp64<0x112, 0xf, 0xf, true>(x);
+  x += dpp64<0x114, 0xf, 0xf, true>(x);
+  x += dpp64<0x118, 0xf, 0xf, true>(x);
+  x += dpp64<0x142, 0xa, 0xf, false>(x);
+  return x + dpp64<0x143, 0xc, 0xf, false>(x);
+}
+__device__ __forceinline__ unsigned long long readlane64(unsigned long long x, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), l);
+  return ((unsigned long long)hi << 32) | lo;
+}
+// x + (x of the lane 8, 16 or 32 apart), in the same pairs as a shuffle butterfly
+template <int OFF>
+__device__ __forceinline__ double add_xor(double x) {
+  static_assert(OFF == 8 || OFF == 16 || OFF == 32, "lane distance");
+  if constexpr (OFF == 8) {
+    return x + dppf64<0x128>(x);   // row_ror:8 within a row of 16
+  } else {
+    const uint32_t lo = (uint32_t)__double_as_longlong(x), hi = (uint32_t)((unsigned long long)__double_as_longlong(x) >> 32);
+    uint32_t a0, a1, b0, b1;
+    if constexpr (OFF == 16) {
+      const auto sl = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+      const auto sh = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+      a0 = sl[0], a1 = sl[1], b0 = sh[0], b1 = sh[1];
+    } else {
+      const auto sl = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+      const auto sh = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+      a0 = sl[0], a1 = sl[1], b0 = sh[0], b1 = sh[1];
+    }
+    return __longlong_as_double((long long)(((unsigned long long)b0 << 32) | a0)) +
+           __longlong_as_double((long long)(((unsigned long long)b1 << 32) | a1));
+  }
+}
+
+// ---------------------------------------------------------------------------------------
 // k_pool: x [BH][N][D] -> mean of every block of `block` tokens (real tokens only), for one
 // or two tensors (Q and K) in one launch.  Item = 16 consecutive blocks of one head of one
 // tensor; grid = (groups of tensor 0 + groups of tensor 1, BH), 256 threads.  Wave w pools
 // blocks w, w+4, w+8, w+12 of the group: lane l reads 16-byte chunk l % CPR of rows
 // l / CPR + RPL*i (16 loads in flight per lane), accumulates in float64 and the lanes of a
-// chunk are summed with cross-lane shuffles.  The 16 pooled rows are staged in LDS and
+// chunk are summed across lanes (DPP and lane swaps).  The 16 pooled rows are staged in LDS and
 // written as one contiguous run: layout 1 is the swizzled float64 MFMA operand order of
 // k_select (blocks past nb written as zero), layout 0 the plain [BH][nb][D] array.
 // ---------------------------------------------------------------------------------------
@@ -55,7 +128,7 @@ struct PoolArgs {
 // Means of the real tokens of NBK blocks j0, j0 + js, ... (block j: tokens [j block,
 // min(j block + block, N))) of one head's rows xh, by one wave: lane l reads 16-byte chunk
 // l % CPR of rows l / CPR + RPL i of every block (NBK x 16 loads in flight per lane),
-// accumulates in float64, and the lanes of a chunk are summed with cross-lane shuffles.  Lanes
+// accumulates in float64, and the lanes of a chunk are summed by lane swaps.  Lanes
 // l < CPR return dims l EPC .. l EPC + EPC - 1 of each block (zero for blocks >= nb).
 template <typename T, int D, int NBK>
 __device__ __forceinline__ void pool_blocks(const T *__restrict__ xh, int j0, int js, int block, int nb, int N,
@@ -100,9 +173,11 @@ __device__ __forceinline__ void pool_blocks(const T *__restrict__ xh, int j0, in
 #pragma unroll
   for (int b = 0; b < NBK; ++b) {
 #pragma unroll
-    for (int off = CPR; off < 64; off <<= 1)
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) acc[b][e] += __shfl_xor(acc[b][e], off);
+    for (int e = 0; e < EPC; ++e) {
+      if constexpr (CPR <= 8) acc[b][e] = add_xor<8>(acc[b][e]);
+      if constexpr (CPR <= 16) acc[b][e] = add_xor<16>(acc[b][e]);
+      acc[b][e] = add_xor<32>(acc[b][e]);
+    }
     const int cnt = e0[b] - s0[b];
 #pragma unroll
     for (int e = 0; e < EPC; ++e) mean[b][e] = cnt > 0 ? acc[b][e] / (double)cnt : 0.0;
@@ -245,14 +320,10 @@ __device__ __forceinline__ void select_row(const Row &ev, int nkb, bool bycnt, u
       m4[q] = bycnt ? (unsigned long long)c4[q] : hm[4 * lane + q];
       ms += m4[q];
     }
-    // mass of the digits held by higher lanes (larger keys)
-    unsigned long long sm = ms;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const unsigned long long o = __shfl_down(sm, off);
-      if (lane + off < 64) sm += o;
-    }
-    unsigned long long acc = above + (sm - ms);
+    // mass of the digits held by higher lanes (larger keys): the total minus the inclusive
+    // prefix over the lanes
+    const unsigned long long pre = wave_scan(ms);
+    unsigned long long acc = above + (readlane64(pre, 63) - pre);
     int dig = -1;
     unsigned long long nab = 0;
     uint32_t cnt = 0;
@@ -272,9 +343,9 @@ __device__ __forceinline__ void select_row(const Row &ev, int nkb, bool bycnt, u
       break;
     }
     const int L = __ffsll((long long)bal) - 1;
-    dig = __shfl(dig, L);
-    above = __shfl(nab, L);
-    cnt = __shfl(cnt, L);
+    dig = __builtin_amdgcn_readlane(dig, L);
+    above = readlane64(nab, L);
+    cnt = (uint32_t)__builtin_amdgcn_readlane((int)cnt, L);
     lo += (unsigned long long)dig << sh;
     width = 1ull << sh;
     ntie = cnt;
@@ -519,8 +590,7 @@ __device__ __forceinline__ void select_item(SelLds<T, D, MAXT, NWV> &L, const Se
   }
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
-#pragma unroll
-    for (int off = 8; off >= 1; off >>= 1) mx[v] = fmax(mx[v], __shfl_xor(mx[v], off, 16));
+    mx[v] = row16_max(mx[v]);
     if (jl == 0) L.part[w][ig + 4 * v] = mx[v];
   }
   __syncthreads();
@@ -549,11 +619,8 @@ __device__ __forceinline__ void select_item(SelLds<T, D, MAXT, NWV> &L, const Se
   }
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
-#pragma unroll
-    for (int off = 8; off >= 1; off >>= 1) {
-      zs[v] += __shfl_xor(zs[v], off, 16);
-      mn[v] = fmin(mn[v], __shfl_xor(mn[v], off, 16));
-    }
+    zs[v] = row16_sum(zs[v]);
+    mn[v] = row16_min(mn[v]);
     if (jl == 0) {
       L.zpart[w][ig + 4 * v] = zs[v];
       L.minpart[w][ig + 4 * v] = mn[v];
