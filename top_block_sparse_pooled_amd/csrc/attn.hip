@@ -602,20 +602,32 @@ __global__ __launch_bounds__(512, 1) void k_attn_pp(
 }
 
 // ---------------------------------------------------------------------------------------
-// float32 attention: one thread per query row, K/V tiles through LDS, online softmax in
-// float32.  grid = rows (tile t processes worklist[t]).
+// float32 attention on the float32 MFMA (v_mfma_f32_32x32x2_f32).  grid = rows (workgroup t
+// processes CSR row worklist[t]); BQ / 32 waves, wave w owns query rows 32 w .. 32 w + 31 of the
+// block.  The row's kept key blocks are walked in tiles of 32 keys staged in LDS, rows padded
+// to D + 1 floats so that the 32 key rows of an operand read fall on distinct banks:
+//   S^T (32 keys x 32 queries) = sum over the D / 2 steps j of K[key][2 j + h] Q[query][2 j + h]
+//   (lane l: key or query l % 32, h = l / 32); online softmax in float32, exp2 with the scale
+//   folded into one FMA; O^T (D x 32 queries) += V^T P, where step s of the product pairs the
+//   two keys that accumulator element s holds in the lower and upper lane halves
+//   (8 (s / 4) + s % 4 and the same + 4), so P feeds the MFMA straight from the S layout.
 // ---------------------------------------------------------------------------------------
 template <int BQ, int BK, int D>
-__global__ __launch_bounds__(BQ) void k_attn_f32(const float *__restrict__ q, const float *__restrict__ k,
-                                                 const float *__restrict__ v, float *__restrict__ o,
-                                                 const int32_t *__restrict__ row_ptr,
-                                                 const int32_t *__restrict__ col_idx,
-                                                 const int32_t *__restrict__ worklist,
-                                                 int32_t *__restrict__ counter, int rows, int nqb, int nkb, int N,
-                                                 float scale, uint64_t *__restrict__ trace) {
-  __shared__ float Kt[BK][D + 1];
-  __shared__ float Vt[BK][D];
-  const int tid = threadIdx.x;
+__global__ __launch_bounds__(BQ * 2) void k_attn_f32(const float *__restrict__ q, const float *__restrict__ k,
+                                                     const float *__restrict__ v, float *__restrict__ o,
+                                                     const int32_t *__restrict__ row_ptr,
+                                                     const int32_t *__restrict__ col_idx,
+                                                     const int32_t *__restrict__ worklist,
+                                                     int32_t *__restrict__ counter, int rows, int nqb, int nkb, int N,
+                                                     float scale, uint64_t *__restrict__ trace) {
+  static_assert(BQ % 32 == 0 && BK % 32 == 0 && D % 32 == 0, "32-row, 32-key and 32-dim tiles");
+  constexpr int NT = BQ * 2;      // threads: BQ / 32 waves
+  constexpr int LD = D + 1;       // padded tile row (floats)
+  constexpr int NM = D / 32;      // 32-dim output tiles
+  __shared__ float Kt[32 * LD];
+  __shared__ float Vt[32 * LD];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, h = lane >> 5;
   const int t = blockIdx.x;
   {
     // consume only a plan built for this launch (float32, one query block per unit, same CSR shape)
@@ -631,47 +643,88 @@ __global__ __launch_bounds__(BQ) void k_attn_f32(const float *__restrict__ q, co
   if (trace != nullptr) t_start = __builtin_amdgcn_s_memrealtime();
   const int row = worklist[t];
   const int bh = row / nqb, qi = row - bh * nqb;
-  const int qrow = qi * BQ + tid;
+  const int qrow = qi * BQ + 32 * w + l32;
   const bool live = qrow < N;
-  float qv[D], acc[D];
+  // this lane's Q operand: Q[qrow][2 j + h]
+  float qv[D / 2];
   const float *qp = q + ((size_t)bh * N + (live ? qrow : 0)) * D;
 #pragma unroll
-  for (int c = 0; c < D; ++c) {
-    qv[c] = live ? qp[c] * scale : 0.f;
-    acc[c] = 0.f;
-  }
+  for (int j = 0; j < D / 2; ++j) qv[j] = live ? qp[2 * j + h] : 0.f;
+  f16v oacc[NM];
+#pragma unroll
+  for (int m = 0; m < NM; ++m)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[m][i] = 0.f;
+  const float sl2 = scale * 1.4426950408889634f;
   float m_run = -INFINITY, l_run = 0.f;
   const int beg = row_ptr[row], end = row_ptr[row + 1];
   const float *kh = k + (size_t)bh * N * D;
   const float *vh = v + (size_t)bh * N * D;
   for (int e = beg; e < end; ++e) {
-    const int key0 = col_idx[e] * BK;
-    const int nk = min(BK, N - key0);
-    __syncthreads();
-    for (int i = tid; i < BK * D; i += BQ) {
-      const int r = i / D, c = i % D;
-      Kt[r][c] = r < nk ? kh[(size_t)(key0 + r) * D + c] : 0.f;
-      Vt[r][c] = r < nk ? vh[(size_t)(key0 + r) * D + c] : 0.f;
-    }
-    __syncthreads();
-    for (int r = 0; r < nk; ++r) {
-      float s = 0.f;
+    const int kb0 = col_idx[e] * BK;
+    for (int tt = 0; tt < BK / 32; ++tt) {
+      const int key0 = kb0 + 32 * tt;
+      if (key0 >= N) break;   // the same for every wave
+      const int nk = min(32, N - key0);
+      __syncthreads();        // the previous tile is consumed
+      for (int i = tid; i < 32 * D; i += NT) {
+        const int r = i / D, c = i % D;
+        Kt[r * LD + c] = r < nk ? kh[(size_t)(key0 + r) * D + c] : 0.f;
+        Vt[r * LD + c] = r < nk ? vh[(size_t)(key0 + r) * D + c] : 0.f;
+      }
+      __syncthreads();
+      f16v sacc = {};
 #pragma unroll
-      for (int c = 0; c < D; ++c) s = fmaf(qv[c], Kt[r][c], s);
-      const float m_new = fmaxf(m_run, s);
-      const float corr = expf(m_run - m_new);
-      const float pexp = expf(s - m_new);
-      l_run = l_run * corr + pexp;
+      for (int j = 0; j < D / 2; ++j)
+        sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(Kt[l32 * LD + 2 * j + h], qv[j], sacc, 0, 0, 0);
+      if (nk < 32) {   // keys past N (the ragged last block) do not take part
 #pragma unroll
-      for (int c = 0; c < D; ++c) acc[c] = fmaf(pexp, Vt[r][c], acc[c] * corr);
+        for (int i = 0; i < 16; ++i)
+          if (8 * (i >> 2) + 4 * h + (i & 3) >= nk) sacc[i] = -INFINITY;
+      }
+      float mloc = sacc[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mloc = fmaxf(mloc, sacc[i]);
+      {
+        auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mloc), __float_as_uint(mloc), false, false);
+        mloc = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      }
+      // the tile holds at least one key below N, so the new maximum is finite
+      const float m_new = fmaxf(m_run, mloc * sl2);
+      const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      float ps = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        sacc[i] = __builtin_amdgcn_exp2f(fmaf(sacc[i], sl2, -m_new));
+        ps += sacc[i];
+      }
+      l_run = l_run * alpha + ps;
       m_run = m_new;
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[m][i] *= alpha;
+#pragma unroll
+      for (int s2 = 0; s2 < 16; ++s2) {
+        const int key = 8 * (s2 >> 2) + 4 * h + (s2 & 3);
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+          oacc[m] = __builtin_amdgcn_mfma_f32_32x32x2f32(Vt[key * LD + 32 * m + l32], sacc[s2], oacc[m], 0, 0, 0);
+      }
     }
   }
+  // the row sum is split between the lane halves (each holds 16 of every 32 keys)
+  auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
+  const float inv = 1.f / (__uint_as_float(sw[0]) + __uint_as_float(sw[1]));
   if (live) {
-    float *op = o + ((size_t)bh * N + qrow) * D;
-    const float inv = 1.f / l_run;
+    // lane: query qrow, dims 32 m + 8 a + 4 h + b
+    float *op = o + ((size_t)bh * N + qrow) * D + 4 * h;
 #pragma unroll
-    for (int c = 0; c < D; ++c) op[c] = acc[c] * inv;
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        *reinterpret_cast<f4 *>(op + 32 * m + 8 * a) =
+            f4{oacc[m][4 * a] * inv, oacc[m][4 * a + 1] * inv, oacc[m][4 * a + 2] * inv, oacc[m][4 * a + 3] * inv};
   }
   if (trace != nullptr && tid == 0) {
     const uint64_t t_end = __builtin_amdgcn_s_memrealtime();
@@ -729,7 +782,7 @@ static int launch_attn_f32_t(const void *q, const void *k, const void *v, void *
                              const int32_t *col_idx, const int32_t *wl, int32_t *counter, int rows, int nqb, int nkb,
                              int N, uint64_t *trace, hipStream_t st) {
   const float scale = (float)(1.0 / sqrt((double)D));
-  hipLaunchKernelGGL((k_attn_f32<BQ, BK, D>), dim3(rows), dim3(BQ), 0, st, (const float *)q, (const float *)k,
+  hipLaunchKernelGGL((k_attn_f32<BQ, BK, D>), dim3(rows), dim3(BQ * 2), 0, st, (const float *)q, (const float *)k,
                      (const float *)v, (float *)o, row_ptr, col_idx, wl, counter, rows, nqb, nkb, N, scale, trace);
   FV_CHECK_LAUNCH();
   return FVATTN_OK;
