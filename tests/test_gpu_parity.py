@@ -92,6 +92,9 @@ SMALL = [
                                                                 "bf16", (21, 30, 35)), 0.85),
     ("bf16_h1_n75600_nkb1182", lambda: workloads.small_case(1, 75600, 128, 64, 64, 27, ("uniform", 0.0, 3.0),
                                                             "bf16", (21, 45, 80)), 0.9),
+    # rows of 2,400 key blocks: the longest rows resolved wholly in registers
+    ("bf16_h1_n76800_bk32_nkb2400", lambda: workloads.small_case(1, 76800, 128, 64, 32, 40, ("uniform", 0.0, 3.0),
+                                                                 "bf16", (20, 48, 80)), 0.9),
     # more heads (B*H = 8, 16, 24)
     ("bf16_h8_n3000", lambda: workloads.small_case(8, 3000, 128, 64, 64, 35, ("uniform", 0.0, 4.0),
                                                          "bf16", (3, 20, 50)), 0.9),

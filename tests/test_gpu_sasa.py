@@ -123,6 +123,9 @@ CASES = [
     ("bf16_h2_n69120_bq128_bk32_nkb2160", lambda: workloads.small_case(2, 69120, 128, 128, 32, 55,
                                                                        ("uniform", 0.5, 3.0), "bf16",
                                                                        (24, 36, 80)), 0.9),
+    ("bf16_h2_n83200_bq128_bk32_nkb2600", lambda: workloads.small_case(2, 83200, 128, 128, 32, 56,
+                                                                       ("uniform", 0.5, 3.0), "bf16",
+                                                                       (20, 52, 80)), 0.9),
 ]
 SETTINGS = [
     ("g2_a0.5", dict(groups=2, alpha=0.5, tau=0.0), {}),

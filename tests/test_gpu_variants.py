@@ -59,6 +59,12 @@ CASES = [
                                                             "bf16", (21, 45, 80))),
     ("bf16_h1_n69120_bk32_nkb2160", lambda: workloads.small_case(1, 69120, 128, 64, 32, 47, ("uniform", 0.0, 3.0),
                                                                  "bf16", (24, 36, 80))),
+    ("bf16_h1_n76800_bk32_nkb2400", lambda: workloads.small_case(1, 76800, 128, 64, 32, 48, ("uniform", 0.0, 3.0),
+                                                                 "bf16", (20, 48, 80))),
+    # rows of 2,600 key blocks: part in registers, part in the scratch
+    ("bf16_h1_n83200_bq128_bk32_nkb2600", lambda: workloads.small_case(1, 83200, 128, 128, 32, 49,
+                                                                       ("uniform", 0.0, 3.0), "bf16",
+                                                                       (20, 52, 80))),
 ]
 
 VARIANTS = [

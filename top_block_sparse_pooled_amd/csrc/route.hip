@@ -83,6 +83,50 @@ __device__ __forceinline__ unsigned long long readlane64(unsigned long long x, i
   const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), l);
   return ((unsigned long long)hi << 32) | lo;
 }
+// the two values of the lane pair 16 or 32 apart (own and partner, in either order)
+template <int OFF>
+__device__ __forceinline__ void lane_pair(unsigned long long x, unsigned long long &p0, unsigned long long &p1) {
+  static_assert(OFF == 16 || OFF == 32, "lane distance");
+  const uint32_t lo = (uint32_t)x, hi = (uint32_t)(x >> 32);
+  if constexpr (OFF == 16) {
+    const auto sl = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    const auto sh = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    p0 = ((unsigned long long)sh[0] << 32) | sl[0];
+    p1 = ((unsigned long long)sh[1] << 32) | sl[1];
+  } else {
+    const auto sl = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+    const auto sh = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+    p0 = ((unsigned long long)sh[0] << 32) | sl[0];
+    p1 = ((unsigned long long)sh[1] << 32) | sl[1];
+  }
+}
+__device__ __forceinline__ double as_f64(unsigned long long x) { return __longlong_as_double((long long)x); }
+__device__ __forceinline__ unsigned long long as_u64(double x) { return (unsigned long long)__double_as_longlong(x); }
+// all-reduce over the 64 lanes: rows of 16, then the row pairs 16 and 32 apart
+__device__ __forceinline__ double wave_max(double x) {
+  unsigned long long a, b;
+  x = row16_max(x);
+  lane_pair<16>(as_u64(x), a, b);
+  x = fmax(as_f64(a), as_f64(b));
+  lane_pair<32>(as_u64(x), a, b);
+  return fmax(as_f64(a), as_f64(b));
+}
+__device__ __forceinline__ double wave_min(double x) {
+  unsigned long long a, b;
+  x = row16_min(x);
+  lane_pair<16>(as_u64(x), a, b);
+  x = fmin(as_f64(a), as_f64(b));
+  lane_pair<32>(as_u64(x), a, b);
+  return fmin(as_f64(a), as_f64(b));
+}
+__device__ __forceinline__ unsigned long long wave_sum(unsigned long long x) {
+  unsigned long long a, b;
+  x = row16_sum(x);
+  lane_pair<16>(x, a, b);
+  x = a + b;
+  lane_pair<32>(x, a, b);
+  return a + b;
+}
 // x + (x of the lane 8, 16 or 32 apart), in the same pairs as a shuffle butterfly
 template <int OFF>
 __device__ __forceinline__ double add_xor(double x) {
@@ -263,19 +307,46 @@ __device__ __forceinline__ unsigned long long fix52(double e) {
 // the bin holds one key or one key value (ties, resolved toward lower indices).  Returns the
 // kept-bit word of key blocks 32 lane .. 32 lane + 31 (zero for lanes past the row) and sets
 // `count` to the number of kept blocks.
-// A row of softmax numerators (lane l: key block l + 64 t): in registers, or in memory (the
-// large select's scratch), read once per pass.
+// A row of softmax numerators (lane l: key block l + 64 t): entries t < kRegs in registers,
+// the rest in memory (the large select's scratch), read again on every pass.
 template <int NPL>
 struct RegRow {
-  static constexpr int kUnroll = NPL;
+  static constexpr int kRegs = NPL;
   const double (&v)[NPL];
-  __device__ __forceinline__ double get(int t) const { return v[t]; }
+  __device__ __forceinline__ double reg(int t) const { return v[t]; }
+  __device__ __forceinline__ double mem(int) const { return 0.0; }
+};
+template <int R>
+struct SplitRow {
+  static constexpr int kRegs = R;
+  const double (&v)[R];
+  const double *p;
+  __device__ __forceinline__ double reg(int t) const { return v[t]; }
+  __device__ __forceinline__ double mem(int t) const { return p[(threadIdx.x & 63) + 64 * t]; }
 };
 struct MemRow {
-  static constexpr int kUnroll = 4;
+  static constexpr int kRegs = 0;
   const double *p;
-  __device__ __forceinline__ double get(int t) const { return p[(threadIdx.x & 63) + 64 * t]; }
+  __device__ __forceinline__ double reg(int) const { return 0.0; }
+  __device__ __forceinline__ double mem(int t) const { return p[(threadIdx.x & 63) + 64 * t]; }
 };
+// f(t, valid, e) over the NPL entries of this lane, in order of t; e is 0 past the row (whose
+// entries are never read)
+template <int NPL, class Row, class F>
+__device__ __forceinline__ void for_row(const Row &ev, int nkb, F &&f) {
+  const int lane = threadIdx.x & 63;
+  constexpr int R = Row::kRegs < NPL ? Row::kRegs : NPL;
+#pragma unroll
+  for (int t = 0; t < R; ++t) {
+    const bool valid = lane + 64 * t < nkb;
+    f(t, valid, valid ? ev.reg(t) : 0.0);
+  }
+#pragma unroll 4
+  for (int t = R; t < NPL; ++t) {
+    const bool valid = lane + 64 * t < nkb;
+    f(t, valid, valid ? ev.mem(t) : 0.0);
+  }
+}
 
 template <int NPL, class Row>
 __device__ __forceinline__ void select_row(const Row &ev, int nkb, bool bycnt, unsigned long long T,
@@ -299,17 +370,14 @@ __device__ __forceinline__ void select_row(const Row &ev, int nkb, bool bycnt, u
     // (LDS operations of one wave take effect in issue order; the fences only keep the
     // compiler from moving them)
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-#pragma unroll Row::kUnroll
-    for (int t = 0; t < NPL; ++t) {
-      const bool valid = lane + 64 * t < nkb;
-      const double e = valid ? ev.get(t) : 0.0;   // entries past the row are never read
+    for_row<NPL>(ev, nkb, [&](int, bool valid, double e) {
       const unsigned long long off = (unsigned long long)__double_as_longlong(e) - lo;
       if (valid && off < width) {
         const int dg = (int)(off >> sh);
         atomicAdd(&hc[dg], 1u);
         if (!bycnt) atomicAdd(&hm[dg], fix52(e));
       }
-    }
+    });
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     unsigned long long m4[4];
     uint32_t c4[4];
@@ -364,10 +432,8 @@ __device__ __forceinline__ void select_row(const Row &ev, int nkb, bool bycnt, u
 #pragma unroll
   for (int q = 0; q < kRowWords; ++q) words[q] = 0u;
   count = 0;
-#pragma unroll Row::kUnroll
-  for (int t = 0; t < NPL; ++t) {
-    const bool valid = lane + 64 * t < nkb;
-    const unsigned long long key = valid ? (unsigned long long)__double_as_longlong(ev.get(t)) : 0ull;
+  for_row<NPL>(ev, nkb, [&](int t, bool valid, double e) {
+    const unsigned long long key = (unsigned long long)__double_as_longlong(e);
     bool keep = valid && (st == 3 || key >= hi || (st == 1 && key >= lo));
     if (st == 2) {
       const bool tie = valid && key == lo;
@@ -381,7 +447,7 @@ __device__ __forceinline__ void select_row(const Row &ev, int nkb, bool bycnt, u
     if (lane == (2 * t) % 64) words[(2 * t) / 64] = (uint32_t)mt;
     if (lane == (2 * t + 1) % 64) words[(2 * t + 1) / 64] = (uint32_t)(mt >> 32);
     count += (int)__popcll(mt);
-  }
+  });
 }
 
 // Arguments of one select item.
@@ -462,9 +528,9 @@ __device__ __forceinline__ void row_decide(const Row &ev, unsigned long long Z, 
   if (EXT && a.sel.imp != nullptr) {
     // importance of every block: the candidates' order for SASA
     const double invz = Z > 0 ? kFix52 / (double)Z : 0.0;   // 1 / Z with Z in 2^-52 units
-#pragma unroll Row::kUnroll
-    for (int t = 0; t < NPL; ++t)
-      if (lane + 64 * t < nkb) a.sel.imp[row * nkb + lane + 64 * t] = ev.get(t) * invz;
+    for_row<NPL>(ev, nkb, [&](int t, bool valid, double e) {
+      if (valid) a.sel.imp[row * nkb + lane + 64 * t] = e * invz;
+    });
   }
 }
 
@@ -713,6 +779,8 @@ struct SelLdsL {
   int cnt[16];
 };
 
+constexpr int kLargeRegNpl = 40;     // rows of up to 2560 key blocks are resolved in registers
+constexpr int kLargeSplitRegs = 32;  // longer rows keep their first 2048 entries there
 template <typename T, int D, int NPL, bool EXT>
 __device__ __forceinline__ void select_item_large(SelLdsL<T, D> &L, const SelArgs &a, double *__restrict__ scr,
                                                   int nkbp, int bh, int g) {
@@ -787,18 +855,36 @@ __device__ __forceinline__ void select_item_large(SelLdsL<T, D> &L, const SelArg
     }
     const size_t row = (size_t)bh * nqb + i;
     double *sr = scr + (size_t)r * nkbp;   // this lane reads and writes entries lane + 64 t only
-    double mx = -INFINITY;
+    // the first R entries per lane are read once into registers, the rest (rows longer than
+    // the registers hold) stay in the scratch and are read again on every pass
+    constexpr int R = NPL <= kLargeRegNpl ? NPL : kLargeSplitRegs;
+    double ev[R];
+#pragma unroll
+    for (int t = 0; t < R; ++t) {
+      const int j = lane + 64 * t;
+      ev[t] = j < nkb ? sr[j] : -INFINITY;
+    }
+    double mx = ev[0];
+#pragma unroll
+    for (int t = 1; t < R; ++t) mx = fmax(mx, ev[t]);
 #pragma unroll 2
-    for (int t = 0; t < NPL; ++t) {
+    for (int t = R; t < NPL; ++t) {
       const int j = lane + 64 * t;
       if (j < nkb) mx = fmax(mx, sr[j]);
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) mx = fmax(mx, __shfl_xor(mx, off));
+    mx = wave_max(mx);
     unsigned long long Z = 0;
     double emin = 1.0;
+#pragma unroll
+    for (int t = 0; t < R; ++t) {
+      const bool valid = lane + 64 * t < nkb;
+      const double e = valid ? exp(ev[t] - mx) : 0.0;
+      ev[t] = e;
+      Z += fix52(e);
+      if (valid) emin = fmin(emin, e);
+    }
 #pragma unroll 2
-    for (int t = 0; t < NPL; ++t) {
+    for (int t = R; t < NPL; ++t) {
       const int j = lane + 64 * t;
       if (j < nkb) {
         const double e = exp(sr[j] - mx);
@@ -807,12 +893,12 @@ __device__ __forceinline__ void select_item_large(SelLdsL<T, D> &L, const SelArg
         emin = fmin(emin, e);
       }
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      Z += __shfl_xor(Z, off);
-      emin = fmin(emin, __shfl_xor(emin, off));
-    }
-    row_decide<NPL, EXT>(MemRow{sr}, Z, emin, i, row, a, L.h_mass[w], L.h_cnt[w], &L.cnt[r]);
+    Z = wave_sum(Z);
+    emin = wave_min(emin);
+    if constexpr (R == NPL)
+      row_decide<NPL, EXT>(RegRow<NPL>{ev}, Z, emin, i, row, a, L.h_mass[w], L.h_cnt[w], &L.cnt[r]);
+    else
+      row_decide<NPL, EXT>(SplitRow<R>{ev, sr}, Z, emin, i, row, a, L.h_mass[w], L.h_cnt[w], &L.cnt[r]);
   }
   __syncthreads();   // row counts in LDS; scratch rows consumed before the next item's scores
   if (w == 0) {
@@ -1030,6 +1116,10 @@ static int launch_route_d(const RouteLaunch &r, hipStream_t st) {
                    sel.imp != nullptr;
   if (r.nkb <= 2048)
     return ext ? launch_route_large<T, D, 32, true>(r, st) : launch_route_large<T, D, 32, false>(r, st);
+  if (r.nkb <= 2368)   // the 720p layer with 32-token key blocks (2,363) without a long spill
+    return ext ? launch_route_large<T, D, 37, true>(r, st) : launch_route_large<T, D, 37, false>(r, st);
+  if (r.nkb <= 2560)
+    return ext ? launch_route_large<T, D, 40, true>(r, st) : launch_route_large<T, D, 40, false>(r, st);
   return ext ? launch_route_large<T, D, 64, true>(r, st) : launch_route_large<T, D, 64, false>(r, st);
 }
 
