@@ -12,8 +12,10 @@
 //                pooled rows in the lane order the float64 MFMA of k_select consumes (one
 //                512-byte load per operand).
 //  * k_select    one item = 16 query blocks of one head (4 waves; 8 above 512 key blocks),
-//                persistent.  The item pools its own query blocks into LDS (same summation
-//                order as k_pool), so the raw Q reads overlap other workgroups' work.  Scores
+//                persistent.  The workgroup pools the query blocks of its next item while it
+//                resolves the rows of the current one (same summation order as k_pool), so
+//                the raw Q reads overlap the radix passes; the first item is pooled before
+//                the loop.  Scores
 //                qbar.kbar^T/sqrt(d) come from v_mfma_f64_16x16x4 and stay in registers (wave
 //                w holds key tiles w, w + NWV, ...).  Softmax numerators e = exp(s - max) in
 //                float64; masses as 2^-52 fixed point so every partial sum is exact and order
@@ -226,6 +228,79 @@ __device__ __forceinline__ void pool_blocks(const T *__restrict__ xh, int j0, in
 #pragma unroll
     for (int e = 0; e < EPC; ++e) mean[b][e] = cnt > 0 ? acc[b][e] / (double)cnt : 0.0;
   }
+}
+
+// One block's mean split in two steps, so that its loads can be in flight while other work
+// runs: pool_issue starts round `base` (rows base .. base + RPR - 1 of the block) of the same
+// loads as pool_blocks, pool_take adds them to the float64 sums.  pool_keep finishes the block
+// (lane swaps, division by the real-token count) and leaves lane l with dims
+// (l % CPR) EPC + (l / CPR) KEEP + k, k < KEEP = D / 64: every dim exactly once over the wave.
+template <typename T, int D>
+struct PoolGeo {
+  static constexpr int EPC = DT<T>::per16, CPR = D / EPC, RPL = 64 / CPR, NLD = 16, RPR = RPL * NLD;
+  static constexpr int KEEP = D / 64;
+};
+template <typename T, int D>
+__device__ __forceinline__ void pool_issue(const T *__restrict__ xh, int j, int block, int nb, int N, int base,
+                                           u32x4 (&buf)[PoolGeo<T, D>::NLD]) {
+  using P = PoolGeo<T, D>;
+  const int lane = threadIdx.x & 63;
+  const int c = lane % P::CPR, r = lane / P::CPR;
+  const int s0 = j < nb ? j * block : 0, e0 = j < nb ? min(s0 + block, N) : 0;
+#pragma unroll
+  for (int i = 0; i < P::NLD; ++i) {
+    const int row = s0 + base + r + P::RPL * i;
+    buf[i] = u32x4{0u, 0u, 0u, 0u};
+    if (row < e0) buf[i] = *reinterpret_cast<const u32x4 *>(xh + (size_t)row * D + c * P::EPC);
+  }
+}
+template <typename T, int D>
+__device__ __forceinline__ void pool_take(const u32x4 (&buf)[PoolGeo<T, D>::NLD], double (&acc)[PoolGeo<T, D>::EPC]) {
+  using P = PoolGeo<T, D>;
+#pragma unroll
+  for (int i = 0; i < P::NLD; ++i) {
+    float f[P::EPC];
+    unpack16(buf[i], f, T());
+#pragma unroll
+    for (int e = 0; e < P::EPC; ++e) acc[e] += (double)f[e];
+  }
+}
+template <typename T, int D>
+__device__ __forceinline__ void pool_keep(int j, int block, int nb, int N, double (&acc)[PoolGeo<T, D>::EPC],
+                                          double (&keep)[PoolGeo<T, D>::KEEP]) {
+  using P = PoolGeo<T, D>;
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int e = 0; e < P::EPC; ++e) {
+    if constexpr (P::CPR <= 8) acc[e] = add_xor<8>(acc[e]);
+    if constexpr (P::CPR <= 16) acc[e] = add_xor<16>(acc[e]);
+    acc[e] = add_xor<32>(acc[e]);
+  }
+  const int s0 = j < nb ? j * block : 0, e0 = j < nb ? min(s0 + block, N) : 0;
+  const int cnt = e0 - s0;
+  const int sel = (lane / P::CPR) * P::KEEP;
+#pragma unroll
+  for (int k = 0; k < P::KEEP; ++k) {
+    double x = acc[0];
+#pragma unroll
+    for (int e = 1; e < P::EPC; ++e) x = (sel + k == e) ? acc[e] : x;
+    keep[k] = cnt > 0 ? x / (double)cnt : 0.0;
+  }
+}
+// The whole block at once (its rounds one after the other).
+template <typename T, int D>
+__device__ __forceinline__ void pool_block_keep(const T *__restrict__ xh, int j, int block, int nb, int N,
+                                                double (&keep)[PoolGeo<T, D>::KEEP]) {
+  using P = PoolGeo<T, D>;
+  double acc[P::EPC];
+#pragma unroll
+  for (int e = 0; e < P::EPC; ++e) acc[e] = 0.0;
+  for (int base = 0; base < block; base += P::RPR) {
+    u32x4 buf[P::NLD];
+    pool_issue<T, D>(xh, j, block, nb, N, base, buf);
+    pool_take<T, D>(buf, acc);
+  }
+  pool_keep<T, D>(j, block, nb, N, acc, keep);
 }
 
 template <typename T, int D>
@@ -552,8 +627,8 @@ struct SelLds {
 
 // One select item: scores, softmax and the Top-p cut (or a routing variant) for query blocks
 // 16 g .. 16 g + 15 of head bh, by the whole workgroup.
-//   1. The item's query blocks are mean-pooled straight into LDS (same summation order as
-//      k_pool); the raw Q reads of one workgroup overlap the compute phases of the others.
+//   1. The item's query blocks, pooled during the previous item's row phase (or before the
+//      first item), are written from registers into LDS.
 //   2. Scores for the 16 rows on the float64 MFMA, wave w holding key tiles w, w + NWV, ...;
 //      row maxima, e = exp(s - max), fixed-point row sums Z and row minima of e across the
 //      waves (two workgroup barriers).
@@ -562,8 +637,11 @@ struct SelLds {
 //      radix passes use a histogram private to the wave, and the kept set leaves as 64-bit
 //      ballots.  No workgroup barrier inside the selection.
 // Outputs counts[row] and the kept-bit mask bitmask[row][nkw]; adds loads to head_load and bsum.
+// pq holds this item's pooled query blocks (this wave's: w, w + NWV, ...) on entry and the next
+// item's (head bhn, group gn) on return; bhn < 0: no next item.
 template <typename T, int D, int MAXT, int NWV, bool EXT>
-__device__ __forceinline__ void select_item(SelLds<T, D, MAXT, NWV> &L, const SelArgs &a, int bh, int g) {
+__device__ __forceinline__ void select_item(SelLds<T, D, MAXT, NWV> &L, const SelArgs &a, int bh, int g,
+                                            double (&pq)[16 / NWV][PoolGeo<T, D>::KEEP], int bhn, int gn) {
   constexpr int KS = D / 4;               // MFMA k-steps
   constexpr int KCAP = SelLds<T, D, MAXT, NWV>::KCAP;
   constexpr int NPL = KCAP / 64;          // values per lane in the row phase
@@ -579,24 +657,18 @@ __device__ __forceinline__ void select_item(SelLds<T, D, MAXT, NWV> &L, const Se
   const int nkt = (nkb + 15) >> 4;
   (void)tid;
 
-  // ---- the item's 16 query blocks, mean-pooled straight into LDS in the float64 MFMA
-  // operand order (block jj, dim c at (c / 4) 64 + jj + 16 (c % 4)); the raw Q reads of one
-  // workgroup overlap the score phases of the others
+  // ---- the item's 16 query blocks, pooled during the previous item's row phase (this wave:
+  // blocks w, w + NWV, ...), into LDS in the float64 MFMA operand order (block jj, dim c at
+  // (c / 4) 64 + jj + 16 (c % 4))
   {
-    const T *xh = reinterpret_cast<const T *>(a.qraw) + (size_t)bh * a.sel.N * D;
-    // two blocks per wave at a time: 32 loads in flight per lane
-    constexpr int NBK = NWV == 4 ? 2 : 1;
-    for (int jj = w; jj < 16; jj += NBK * NWV) {
-      double m[NBK][EPC];
-      pool_blocks<T, D, NBK>(xh, 16 * g + jj, NWV, a.sel.bq, nqb, a.sel.N, m);
-      if (lane < CPR) {
+    using P = PoolGeo<T, D>;
 #pragma unroll
-        for (int b = 0; b < NBK; ++b)
+    for (int k = 0; k < 16 / NWV; ++k) {
+      const int jj = w + NWV * k;
 #pragma unroll
-          for (int e = 0; e < EPC; ++e) {
-            const int cc = lane * EPC + e;
-            L.eq[(cc >> 2) * 64 + jj + b * NWV + 16 * (cc & 3)] = m[b][e];
-          }
+      for (int kk = 0; kk < P::KEEP; ++kk) {
+        const int cc = (lane % P::CPR) * P::EPC + (lane / P::CPR) * P::KEEP + kk;
+        L.eq[(cc >> 2) * 64 + jj + 16 * (cc & 3)] = pq[k][kk];
       }
     }
   }
@@ -703,26 +775,48 @@ __device__ __forceinline__ void select_item(SelLds<T, D, MAXT, NWV> &L, const Se
       for (int v = b * RB / 4; v < (b + 1) * RB / 4; ++v) s_e[ig + 4 * v - b * RB][j] = acc[k][v];
     }
     __syncthreads();
-    // ---- selection: wave w resolves rows b RB + rr NWV + w
+    // ---- selection: wave w resolves rows b RB + rr NWV + w; beside each row it pools one
+    // of its blocks of the next item (its loads in flight during the row's radix passes)
     for (int rr = 0; rr < RPW; ++rr) {
       const int r = b * RB + rr * NWV + w;
       const int i = 16 * g + r;
-      if (i >= nqb) {   // wave-uniform
-        if (lane == 0) L.cnt[r] = 0;
-        continue;
-      }
-      const size_t row = (size_t)bh * nqb + i;
-      double ev[NPL];
+      using P = PoolGeo<T, D>;
+      const int jn = 16 * gn + w + NWV * (b * RPW + rr);   // next item's block (query block index)
+      const T *xn = reinterpret_cast<const T *>(a.qraw) + (size_t)(bhn < 0 ? 0 : bhn) * a.sel.N * D;
+      u32x4 pbuf[P::NLD];
+      if (bhn >= 0) pool_issue<T, D>(xn, jn, a.sel.bq, nqb, a.sel.N, 0, pbuf);
+      if (i < nqb) {   // wave-uniform
+        const size_t row = (size_t)bh * nqb + i;
+        double ev[NPL];
 #pragma unroll
-      for (int t = 0; t < NPL; ++t) ev[t] = s_e[r - b * RB][lane + 64 * t];
-      unsigned long long Z = 0;
-      double emin = 1.0;
+        for (int t = 0; t < NPL; ++t) ev[t] = s_e[r - b * RB][lane + 64 * t];
+        unsigned long long Z = 0;
+        double emin = 1.0;
 #pragma unroll
-      for (int ww = 0; ww < NWV; ++ww) {
-        Z += L.zpart[ww][r];
-        emin = fmin(emin, L.minpart[ww][r]);
+        for (int ww = 0; ww < NWV; ++ww) {
+          Z += L.zpart[ww][r];
+          emin = fmin(emin, L.minpart[ww][r]);
+        }
+        row_decide<NPL, EXT>(RegRow<NPL>{ev}, Z, emin, i, row, a, L.h_mass[w], L.h_cnt[w], &L.cnt[r]);
+      } else if (lane == 0) {
+        L.cnt[r] = 0;
       }
-      row_decide<NPL, EXT>(RegRow<NPL>{ev}, Z, emin, i, row, a, L.h_mass[w], L.h_cnt[w], &L.cnt[r]);
+      if (bhn >= 0) {
+        double pacc[P::EPC];
+#pragma unroll
+        for (int e = 0; e < P::EPC; ++e) pacc[e] = 0.0;
+        pool_take<T, D>(pbuf, pacc);
+        for (int base = P::RPR; base < a.sel.bq; base += P::RPR) {   // blocks longer than one round
+          pool_issue<T, D>(xn, jn, a.sel.bq, nqb, a.sel.N, base, pbuf);
+          pool_take<T, D>(pbuf, pacc);
+        }
+        // rotate: after all of this wave's rows, pq[k] holds block w + NWV k
+#pragma unroll
+        for (int k = 0; k + 1 < 16 / NWV; ++k)
+#pragma unroll
+          for (int kk = 0; kk < P::KEEP; ++kk) pq[k][kk] = pq[k + 1][kk];
+        pool_keep<T, D>(jn, a.sel.bq, nqb, a.sel.N, pacc, pq[16 / NWV - 1]);
+      }
     }
     __syncthreads();   // staged rows and partial sums consumed before they are overwritten
   }
@@ -757,9 +851,21 @@ __global__ __launch_bounds__(64 * NWV, NWV == 4 ? 2 : 1) void k_select(SelArgs a
   const int xcd = blockIdx.x & 7;
   const int nwx = ((int)gridDim.x - xcd + 7) >> 3;
   const int it_end = (int)((long long)items * (xcd + 1) / 8);
-  for (int it = (int)((long long)items * xcd / 8) + (int)(blockIdx.x >> 3); it < it_end; it += nwx) {
+  const int it0 = (int)((long long)items * xcd / 8) + (int)(blockIdx.x >> 3);
+  // the first item's query blocks, pooled here; each item pools the next one's
+  double pq[16 / NWV][PoolGeo<T, D>::KEEP];
+  if (it0 < it_end) {
+    const int bh = it0 / nqg, g = it0 - bh * nqg;
+    const T *xh = reinterpret_cast<const T *>(a.qraw) + (size_t)bh * a.sel.N * D;
+    const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+#pragma unroll
+    for (int k = 0; k < 16 / NWV; ++k) pool_block_keep<T, D>(xh, 16 * g + w + NWV * k, a.sel.bq, a.nqb, a.sel.N, pq[k]);
+  }
+  for (int it = it0; it < it_end; it += nwx) {
     const int bh = it / nqg, g = it - bh * nqg;
-    select_item<T, D, MAXT, NWV, EXT>(L, a, bh, g);
+    const int itn = it + nwx;
+    const int bhn = itn < it_end ? itn / nqg : -1, gn = itn < it_end ? itn - (itn / nqg) * nqg : 0;
+    select_item<T, D, MAXT, NWV, EXT>(L, a, bh, g, pq, bhn, gn);
   }
 }
 
