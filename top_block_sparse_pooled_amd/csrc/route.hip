@@ -649,11 +649,10 @@ __device__ __forceinline__ void select_item(SelLds<T, D, MAXT, NWV> &L, const Se
   constexpr int NB = 16 / RB;
   constexpr int RPW = RB / NWV;           // rows per wave per batch
   static_assert(KCAP % 64 == 0 && RB % NWV == 0 && (RB / 4) * 4 == RB, "row phase geometry");
-  constexpr int EPC = DT<T>::per16, CPR = D / EPC;
   double(*s_e)[KCAP] = reinterpret_cast<double(*)[KCAP]>(L.eq);
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int nqb = a.nqb, nkb = a.nkb, nkw = a.nkw;
+  const int nqb = a.nqb, nkb = a.nkb;
   const int nkt = (nkb + 15) >> 4;
   (void)tid;
 
